@@ -1,0 +1,463 @@
+"""Pins of the float64 oracle against facts fixed outside it.
+
+Each test checks one oracle function against something other than itself:
+values worked by hand from the pages (tests/golden), brute-force loops on tiny
+inputs, a library routine the definition reduces to (torch float64 on the CPU),
+closed forms and invariants.  No GPU is used.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as tF
+
+from oracle import wan_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def T(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+# ----------------------------------------------------------------------------- patchify
+def test_patch_gather_brute_force():
+    B, C, F, H, W = 2, 3, 2, 4, 6
+    u = rng.standard_normal((B, C, F, H, W))
+    got = O.patch_gather(u)
+    for b in range(B):
+        for f in range(F):
+            for i in range(H // 2):
+                for j in range(W // 2):
+                    l = (f * (H // 2) + i) * (W // 2) + j
+                    for c in range(C):
+                        for a in range(2):
+                            for bb in range(2):
+                                assert got[b, l, c * 4 + a * 2 + bb] == u[b, c, f, 2 * i + a, 2 * j + bb]
+
+
+def test_patchify_is_conv3d_kernel_stride_122():
+    B, C, F, H, W, D = 2, 5, 3, 6, 8, 7
+    u = rng.standard_normal((B, C, F, H, W))
+    w = rng.standard_normal((D, C * 4))
+    bias = rng.standard_normal(D)
+    got = O.patchify(u[:, :3], u[:, 3:], w, bias)
+    ref = tF.conv3d(T(u), T(w).reshape(D, C, 1, 2, 2), T(bias), stride=(1, 2, 2))
+    ref = ref.permute(0, 2, 3, 4, 1).reshape(B, -1, D).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_patch_scatter_inverts_gather():
+    u = rng.standard_normal((2, 16, 3, 6, 10))
+    np.testing.assert_array_equal(O.patch_scatter(O.patch_gather(u), 3, 6, 10), u)
+
+
+def test_latent_shapes_golden():
+    g = load_golden("latent_shapes.json")
+    for case in g["cases"]:
+        t, h, w = case["pixels"]
+        lat = [1 + (t - 1) // 4, h // 8, w // 8]
+        assert lat == case["latent"]
+        grid = [lat[0], lat[1] // 2, lat[2] // 2]
+        assert grid == case["grid"]
+        u = np.zeros((1, 16, *lat))
+        assert O.patch_gather(u).shape == (1, case["tokens"], 64)
+        assert O.grid_positions(grid).shape[0] == case["tokens"]
+
+
+# ----------------------------------------------------------------------------- time MLP
+def test_sinusoid_closed_forms():
+    s = O.timestep_sinusoid(500.0)
+    assert s.shape == (256,)
+    np.testing.assert_allclose(s[:128] ** 2 + s[128:] ** 2, 1.0, rtol=0, atol=1e-15)
+    s0 = O.timestep_sinusoid(0.0)
+    np.testing.assert_array_equal(s0[:128], 1.0)
+    np.testing.assert_array_equal(s0[128:], 0.0)
+    # one entry by hand: k = 5, frequency 10000^(-5/128)
+    assert s[5] == pytest.approx(math.cos(500.0 * 10000.0 ** (-5 / 128)), abs=1e-14)
+    assert s[128 + 5] == pytest.approx(math.sin(500.0 * 10000.0 ** (-5 / 128)), abs=1e-14)
+    # k = 0 has frequency 1
+    assert s[0] == pytest.approx(math.cos(500.0), abs=1e-14)
+
+
+def test_time_modulation_brute_force():
+    D = 3
+    w1, b1 = rng.standard_normal((D, 256)), rng.standard_normal(D)
+    w2, b2 = rng.standard_normal((D, D)), rng.standard_normal(D)
+    wm, bm = rng.standard_normal((6 * D, D)), rng.standard_normal(6 * D)
+    tau = 321.0
+    s = [math.cos(tau * 10000.0 ** (-k / 128)) for k in range(128)] + \
+        [math.sin(tau * 10000.0 ** (-k / 128)) for k in range(128)]
+    silu = lambda v: v / (1 + math.exp(-v))
+    h = [silu(sum(w1[n, k] * s[k] for k in range(256)) + b1[n]) for n in range(D)]
+    e = [sum(w2[n, k] * h[k] for k in range(D)) + b2[n] for n in range(D)]
+    se = [silu(v) for v in e]
+    mod = [sum(wm[n, k] * se[k] for k in range(D)) + bm[n] for n in range(6 * D)]
+    got = O.time_modulation(tau, w1, b1, w2, b2, wm, bm)
+    assert got.shape == (6, D)
+    np.testing.assert_allclose(got.ravel(), mod, rtol=1e-12, atol=1e-12)
+    assert O.silu(0.0) == 0.0
+
+
+# ----------------------------------------------------------------------------- norms, GELU
+def test_layer_norm_matches_torch_and_moments():
+    x = rng.standard_normal((5, 7, 96)) * 3 + 1.5
+    got = O.layer_norm(x)
+    ref = tF.layer_norm(T(x), (96,), eps=1e-6).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got.mean(-1), 0.0, atol=1e-12)
+    var = (got ** 2).mean(-1)
+    np.testing.assert_allclose(var, 1.0 - 1e-6 / (x.var(-1) + 1e-6), rtol=1e-10)
+
+
+def test_modulate_reduces_to_layer_norm():
+    x = rng.standard_normal((4, 64))
+    xn = O.layer_norm(x)
+    np.testing.assert_array_equal(O.modulate(xn, np.zeros(64), np.zeros(64)), xn)
+    # (gamma + 1) * f + beta with gamma = 1, beta = 2: 2 f + 2
+    np.testing.assert_allclose(O.modulate(xn, 2.0 * np.ones(64), np.ones(64)), 2 * xn + 2)
+
+
+def test_gelu_exact_form():
+    u = np.linspace(-8, 8, 2001)
+    ref = tF.gelu(T(u), approximate="none").numpy()
+    np.testing.assert_allclose(O.gelu(u), ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(O.gelu(u) - O.gelu(-u), u, rtol=1e-13, atol=1e-14)
+    # the tanh approximation differs visibly: the exact form is the one pinned
+    tanh = tF.gelu(T(u), approximate="tanh").numpy()
+    assert np.max(np.abs(tanh - ref)) > 1e-4
+
+
+# ----------------------------------------------------------------------------- RoPE
+def test_rope_sections():
+    assert O.rope_sections(128) == (44, 42, 42)
+    assert O.rope_sections(64) == (24, 20, 20)
+    assert O.rope_sections(6) == (2, 2, 2)
+
+
+def test_rope_golden_d6():
+    g = load_golden("rope_d6_example.json")
+    grid = tuple(g["grid"])
+    L = grid[0] * grid[1] * grid[2]
+    for inp, out in zip(g["inputs"], g["outputs"]):
+        x = np.zeros((1, L, 1, 6))
+        x[0, g["token"], 0] = inp
+        got = O.rope_apply(x, grid)[0, g["token"], 0]
+        np.testing.assert_allclose(got, out, rtol=0, atol=1e-15)
+
+
+def _rope_complex_torch(x, grid):
+    """RoPE as complex multiplication (a library formulation, independent of the oracle)."""
+    B, L, H, d = x.shape
+    F, Hh, Ww = grid
+    ds = 2 * (d // 6)
+    secs = [d - 2 * ds, ds, ds]
+    f, i, j = torch.meshgrid(torch.arange(F), torch.arange(Hh), torch.arange(Ww), indexing="ij")
+    pos = [f.reshape(-1).double(), i.reshape(-1).double(), j.reshape(-1).double()]
+    angles = []
+    for p, da in zip(pos, secs):
+        inv = 1.0 / (10000.0 ** (torch.arange(0, da, 2, dtype=torch.float64) / da))
+        angles.append(torch.outer(p, inv))
+    ang = torch.cat(angles, dim=1)                       # (L, d/2)
+    rot = torch.polar(torch.ones_like(ang), ang)
+    xc = torch.view_as_complex(T(x).reshape(B, L, H, d // 2, 2).contiguous())
+    return torch.view_as_real(xc * rot[None, :, None, :]).reshape(B, L, H, d).numpy()
+
+
+@pytest.mark.parametrize("d,grid", [(128, (3, 4, 5)), (64, (2, 8, 8)), (6, (2, 3, 4))])
+def test_rope_matches_complex_rotation(d, grid):
+    L = grid[0] * grid[1] * grid[2]
+    x = rng.standard_normal((2, L, 3, d))
+    np.testing.assert_allclose(O.rope_apply(x, grid), _rope_complex_torch(x, grid),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_rope_norm_identity_and_relative_position():
+    grid = (4, 5, 6)
+    L = 4 * 5 * 6
+    d = 128
+    x = rng.standard_normal((1, L, 2, d))
+    r = O.rope_apply(x, grid)
+    # norm of every pair (hence of every head vector) preserved
+    np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_allclose(r[..., 0::2] ** 2 + r[..., 1::2] ** 2,
+                               x[..., 0::2] ** 2 + x[..., 1::2] ** 2, rtol=1e-12, atol=1e-14)
+    # token 0 sits at position (0, 0, 0): unchanged
+    np.testing.assert_array_equal(r[0, 0], x[0, 0])
+    # <R(p) q, R(p') k> = <R(p - p') q, k>
+    pos = O.grid_positions(grid)
+    q = rng.standard_normal(d)
+    k = rng.standard_normal(d)
+    for p_idx, pp_idx in [(119, 0), (119, 37), (64, 31), (77, 77)]:
+        delta = pos[p_idx] - pos[pp_idx]
+        if np.any(delta < 0):
+            continue
+        dd = int((delta[0] * 5 + delta[1]) * 6 + delta[2])
+        rq = O.rope_apply(q.reshape(1, 1, 1, d), grid, rows=[p_idx]).ravel()
+        rk = O.rope_apply(k.reshape(1, 1, 1, d), grid, rows=[pp_idx]).ravel()
+        rqd = O.rope_apply(q.reshape(1, 1, 1, d), grid, rows=[dd]).ravel()
+        assert np.dot(rq, rk) == pytest.approx(np.dot(rqd, k), rel=1e-11, abs=1e-11)
+
+
+# ----------------------------------------------------------------------------- attention
+def test_attention_brute_force():
+    Lq, Lk, d = 3, 5, 4
+    q, k, v = rng.standard_normal((Lq, d)), rng.standard_normal((Lk, d)), rng.standard_normal((Lk, d))
+    out = np.zeros((Lq, d))
+    for i in range(Lq):
+        s = [sum(q[i, t] * k[j, t] for t in range(d)) / math.sqrt(d) for j in range(Lk)]
+        e = [math.exp(x) for x in s]
+        z = sum(e)
+        for c in range(d):
+            out[i, c] = sum(e[j] / z * v[j, c] for j in range(Lk))
+    np.testing.assert_allclose(O.attention(q, k, v), out, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_matches_torch_sdpa_and_chunking():
+    q = rng.standard_normal((2, 3, 70, 32)) * 2
+    k = rng.standard_normal((2, 3, 90, 32)) * 2
+    v = rng.standard_normal((2, 3, 90, 32))
+    ref = tF.scaled_dot_product_attention(T(q), T(k), T(v)).numpy()
+    for b in range(2):
+        for h in range(3):
+            np.testing.assert_allclose(O.attention(q[b, h], k[b, h], v[b, h], chunk=16), ref[b, h],
+                                       rtol=1e-11, atol=1e-12)
+
+
+def test_attention_invariants():
+    q = rng.standard_normal((11, 16)) * 3
+    k = rng.standard_normal((23, 16)) * 3
+    v = rng.standard_normal((23, 16))
+    # softmax rows sum to one: attention to all-ones values gives ones
+    np.testing.assert_allclose(O.attention(q, k, np.ones((23, 16))), 1.0, rtol=1e-13)
+    # all keys equal -> mean of the values
+    kk = np.tile(k[:1], (23, 1))
+    np.testing.assert_allclose(O.attention(q, kk, v), np.tile(v.mean(0), (11, 1)), rtol=1e-12, atol=1e-13)
+    # one key -> that value
+    np.testing.assert_allclose(O.attention(q, k[:1], v[:1]), np.tile(v[:1], (11, 1)), rtol=1e-13)
+    # joint permutation of keys and values changes nothing
+    perm = rng.permutation(23)
+    np.testing.assert_allclose(O.attention(q, k[perm], v[perm]), O.attention(q, k, v), rtol=1e-12)
+    # a planted key far above the rest takes all the weight (max subtraction is stable)
+    k2 = k.copy()
+    k2[7] = q.mean(0) * 1000.0
+    np.testing.assert_allclose(O.attention(q.mean(0, keepdims=True), k2, v), v[7:8], rtol=1e-9)
+
+
+def test_multihead_head_slices():
+    B, L, D, H = 2, 9, 24, 3
+    q, k, v = (rng.standard_normal((B, L, D)) for _ in range(3))
+    ref = tF.scaled_dot_product_attention(T(q).reshape(B, L, H, 8).transpose(1, 2),
+                                          T(k).reshape(B, L, H, 8).transpose(1, 2),
+                                          T(v).reshape(B, L, H, 8).transpose(1, 2))
+    ref = ref.transpose(1, 2).reshape(B, L, D).numpy()
+    np.testing.assert_allclose(O.multihead_attention(q, k, v, H), ref, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- block
+def _tiny_weights(D, F, img, scale=0.3):
+    w = {}
+    shapes = {"qkv": (3 * D, D), "o": (D, D), "cq": (D, D), "ckv": (2 * D, D), "co": (D, D),
+              "ff1": (F, D), "ff2": (D, F)}
+    if img:
+        shapes["ikv"] = (2 * D, D)
+    for n, s in shapes.items():
+        w[n + "_w"] = rng.standard_normal(s) * scale
+        w[n + "_b"] = rng.standard_normal(s[0]) * scale
+    return w
+
+
+def _block_torch(x, mod, ctx, w, H, grid, img_len):
+    """The block composed from torch float64 library ops (independent of the oracle)."""
+    x, ctx, mod = T(x), T(ctx), T(mod)
+    W = {k: T(v) for k, v in w.items()}
+    B, L, D = x.shape
+    d = D // H
+    ln = lambda t: tF.layer_norm(t, (D,), eps=1e-6)
+    sh1, sc1, g1, sh2, sc2, g2 = [mod[:, i][:, None] for i in range(6)]
+
+    def heads(t):
+        return t.reshape(B, t.shape[1], H, d)
+
+    m = ln(x) * (1 + sc1) + sh1
+    qkv = tF.linear(m, W["qkv_w"], W["qkv_b"])
+    q, k, v = qkv.split(D, dim=-1)
+    q = T(_rope_complex_torch(heads(q).numpy(), grid))
+    k = T(_rope_complex_torch(heads(k).numpy(), grid))
+    a = tF.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), heads(v).transpose(1, 2))
+    sa = tF.linear(a.transpose(1, 2).reshape(B, L, D), W["o_w"], W["o_b"])
+    x = x + g1 * sa
+    qc = heads(tF.linear(ln(x), W["cq_w"], W["cq_b"])).transpose(1, 2)
+    kvt = tF.linear(ctx[:, img_len:], W["ckv_w"], W["ckv_b"])
+    kt, vt = kvt.split(D, dim=-1)
+    ca = tF.scaled_dot_product_attention(qc, heads(kt).transpose(1, 2), heads(vt).transpose(1, 2))
+    if img_len:
+        kvi = tF.linear(ctx[:, :img_len], W["ikv_w"], W["ikv_b"])
+        ki, vi = kvi.split(D, dim=-1)
+        ca = ca + tF.scaled_dot_product_attention(qc, heads(ki).transpose(1, 2), heads(vi).transpose(1, 2))
+    x = x + tF.linear(ca.transpose(1, 2).reshape(B, L, D), W["co_w"], W["co_b"])
+    m2 = ln(x) * (1 + sc2) + sh2
+    y = tF.linear(tF.gelu(tF.linear(m2, W["ff1_w"], W["ff1_b"])), W["ff2_w"], W["ff2_b"])
+    return (x + g2 * y).numpy()
+
+
+@pytest.mark.parametrize("img_len", [0, 5])
+def test_block_matches_torch_composition(img_len):
+    B, H, d, F = 2, 2, 12, 40
+    D = H * d
+    grid = (2, 3, 2)
+    L = 12
+    x = rng.standard_normal((B, L, D))
+    mod = rng.standard_normal((B, 6, D)) * 0.5
+    ctx = rng.standard_normal((B, img_len + 7, D))
+    w = _tiny_weights(D, F, img_len > 0)
+    got = O.dit_block(x, mod, ctx, w, H, grid, img_len)
+    ref = _block_torch(x, mod, ctx, w, H, grid, img_len)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+    # the row-sampled form gives the same rows
+    rows = [0, 5, 11]
+    np.testing.assert_allclose(O.dit_block(x, mod, ctx, w, H, grid, img_len, rows=rows), got[:, rows],
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_block_identity_when_gates_and_cross_out_are_zero():
+    B, H, d, F = 1, 2, 12, 40
+    D = H * d
+    grid = (2, 2, 3)
+    x = rng.standard_normal((B, 12, D))
+    mod = rng.standard_normal((B, 6, D))
+    mod[:, 2] = 0.0
+    mod[:, 5] = 0.0
+    w = _tiny_weights(D, F, False)
+    w["co_w"][:] = 0.0
+    w["co_b"][:] = 0.0
+    ctx = rng.standard_normal((B, 7, D))
+    np.testing.assert_array_equal(O.dit_block(x, mod, ctx, w, H, grid), x)
+
+
+def test_block_sublayer_isolation():
+    """Zeroing two of the three sublayers leaves exactly the third's increment."""
+    B, H, d, F = 1, 2, 12, 40
+    D = H * d
+    grid = (2, 2, 3)
+    x = rng.standard_normal((B, 12, D))
+    ctx = rng.standard_normal((B, 7, D))
+    mod = rng.standard_normal((B, 6, D)) * 0.5
+    w = _tiny_weights(D, F, False)
+    # self-attention alone: g2 = 0, W_co = b_co = 0
+    m = mod.copy(); m[:, 5] = 0
+    w0 = dict(w); w0["co_w"] = 0 * w["co_w"]; w0["co_b"] = 0 * w["co_b"]
+    delta = O.dit_block(x, m, ctx, w0, H, grid) - x
+    sa = O.self_attention(O.modulate(O.layer_norm(x), m[:, 0][:, None], m[:, 1][:, None]), w, H, grid)
+    np.testing.assert_allclose(delta, m[:, 2][:, None] * sa, rtol=1e-12, atol=1e-13)
+    # cross-attention alone: g1 = g2 = 0
+    m = mod.copy(); m[:, 2] = 0; m[:, 5] = 0
+    delta = O.dit_block(x, m, ctx, w, H, grid) - x
+    ca = O.cross_attention(O.layer_norm(x), ctx, w, H, 0)
+    np.testing.assert_allclose(delta, ca, rtol=1e-12, atol=1e-13)
+
+
+def test_decoupled_cross_attention_reductions():
+    B, H, D = 1, 2, 16
+    xn = rng.standard_normal((B, 9, D))
+    w = _tiny_weights(D, 8, True)
+    txt = rng.standard_normal((B, 6, D))
+    img = rng.standard_normal((B, 4, D))
+    # no image tokens: the text-only form
+    a0 = O.cross_attention(xn, txt, w, H, 0)
+    # with image tokens: text part + image part share the query and the output projection
+    a1 = O.cross_attention(xn, np.concatenate([img, txt], 1), w, H, 4)
+    wi = dict(w); wi["ckv_w"] = w["ikv_w"]; wi["ckv_b"] = w["ikv_b"]
+    ai = O.cross_attention(xn, img, wi, H, 0)
+    # a1 = (A_t + A_i) W_co^T + b_co = a0 + ai - b_co
+    np.testing.assert_allclose(a1, a0 + ai - w["co_b"], rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- head, CFG, Euler, step
+def test_head_matches_torch():
+    x = rng.standard_normal((2, 10, 32))
+    w, b = rng.standard_normal((64, 32)), rng.standard_normal(64)
+    ref = tF.linear(tF.layer_norm(T(x), (32,), eps=1e-6), T(w), T(b)).numpy()
+    np.testing.assert_allclose(O.head(x, w, b), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_cfg_euler_golden_and_special_cases():
+    g = load_golden("cfg_euler_example.json")
+    v = O.cfg_combine(np.array(g["v_cond"]), np.array(g["v_null"]), g["guide_scale"])
+    np.testing.assert_allclose(v, g["v"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(O.euler_update(np.array(g["z"]), v, g["dt"]), g["z_next"], atol=1e-14)
+    vc, vu = rng.standard_normal(50), rng.standard_normal(50)
+    np.testing.assert_allclose(O.cfg_combine(vc, vu, 1.0), vc, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(O.cfg_combine(vc, vu, 0.0), vu)
+    np.testing.assert_array_equal(O.cfg_combine(vu, vu, 7.5), vu)
+
+
+def test_euler_known_velocities():
+    z0 = rng.standard_normal(100)
+    x1 = rng.standard_normal(100)
+    # constant velocity over a 20-step uniform schedule: z + v
+    v = rng.standard_normal(100)
+    z = z0.copy()
+    for _ in range(20):
+        z = O.euler_update(z, v, 1.0 / 20)
+    np.testing.assert_allclose(z, z0 + v, rtol=1e-12, atol=1e-13)
+    # the straight path from noise x0 to data x1 has velocity x1 - x0: Euler lands on x1
+    z = z0.copy()
+    for _ in range(20):
+        z = O.euler_update(z, x1 - z0, 1.0 / 20)
+    np.testing.assert_allclose(z, x1, rtol=1e-12, atol=1e-13)
+
+
+def _tiny_model(D, cin, img):
+    mw = {"pe_w": rng.standard_normal((D, cin * 4)) * 0.2, "pe_b": rng.standard_normal(D) * 0.2,
+          "t1_w": rng.standard_normal((D, 256)) * 0.1, "t1_b": rng.standard_normal(D) * 0.1,
+          "t2_w": rng.standard_normal((D, D)) * 0.2, "t2_b": rng.standard_normal(D) * 0.2,
+          "m_w": rng.standard_normal((6 * D, D)) * 0.2, "m_b": rng.standard_normal(6 * D) * 0.2,
+          "hd_w": rng.standard_normal((64, D)) * 0.2, "hd_b": rng.standard_normal(64) * 0.2}
+    return mw
+
+
+def test_step_with_identity_blocks_reduces_to_head_of_patchify():
+    D, H = 24, 2
+    z = rng.standard_normal((1, 16, 2, 4, 6))
+    mw = _tiny_model(D, 16, False)
+    # make both gates vanish: zero the gate rows of the modulation layer
+    mw["m_w"][2 * D:3 * D] = 0; mw["m_b"][2 * D:3 * D] = 0
+    mw["m_w"][5 * D:6 * D] = 0; mw["m_b"][5 * D:6 * D] = 0
+    blocks = []
+    for _ in range(2):
+        w = _tiny_weights(D, 32, False)
+        w["co_w"][:] = 0; w["co_b"][:] = 0
+        blocks.append(w)
+    ctx_c, ctx_n = rng.standard_normal((1, 5, D)), rng.standard_normal((1, 5, D))
+    x = O.patchify(z, None, mw["pe_w"], mw["pe_b"])
+    v = O.patch_scatter(O.head(x, mw["hd_w"], mw["hd_b"]), 2, 4, 6)
+    for g in (0.0, 1.0, 5.0):
+        z1 = O.denoise_step(z, None, ctx_c, ctx_n, mw, blocks, H, 500.0, 0.05, g)
+        np.testing.assert_allclose(z1, z + 0.05 * v, rtol=1e-12, atol=1e-13)
+
+
+def test_step_guidance_linearity():
+    D, H = 24, 2
+    z = rng.standard_normal((1, 16, 2, 4, 4))
+    mw = _tiny_model(D, 16, False)
+    blocks = [_tiny_weights(D, 32, False)]
+    ctx_c, ctx_n = rng.standard_normal((1, 5, D)), rng.standard_normal((1, 5, D))
+    zs = {g: O.denoise_step(z, None, ctx_c, ctx_n, mw, blocks, H, 250.0, 0.05, g) for g in (0.0, 1.0, 5.0)}
+    np.testing.assert_allclose(zs[5.0] - zs[0.0], 5 * (zs[1.0] - zs[0.0]), rtol=1e-9, atol=1e-12)
+    # equal contexts: guidance has no effect
+    a = O.denoise_step(z, None, ctx_c, ctx_c, mw, blocks, H, 250.0, 0.05, 5.0)
+    b = O.denoise_step(z, None, ctx_c, ctx_c, mw, blocks, H, 250.0, 0.05, 0.0)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    # g = 1 is the conditional branch alone
+    v_c = O.dit_forward(z, None, ctx_c, mw, blocks, H, 250.0)
+    np.testing.assert_allclose(zs[1.0], z + 0.05 * v_c, rtol=1e-12, atol=1e-13)
