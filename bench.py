@@ -1,0 +1,197 @@
+"""Throughput of one Wan2.1 CFG denoise step on one MI355X.
+
+One step = the whole hot path on the 1.3B 480p x 81-frame workload: patchify,
+time modulation, 30 DiT blocks over the CFG batch of two (cond + null text
+context), the head, guidance and the Euler update (wan_denoise_step).  Inputs
+and weights are seeded synthetic tensors of the real shapes, resident in HBM
+before the timed region.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config wan13b_step] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from video_diffusion_transformer_forward_amd import synth as S  # noqa: E402
+
+MI355X_BF16_TFLOPS = 2516.6   # dense bf16 MFMA peak (256 CU x 4096 flop/clk x 2.4 GHz)
+MI355X_FP32_TFLOPS = 157.3
+METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
+
+
+def block_flops(cfg: S.WanConfig, batch: int) -> dict:
+    """Algorithmic FLOPs of one block over `batch` videos: 2MNK per GEMM, 4 Lq Lk D per attention."""
+    L, D, F, Lt, Li = cfg.seq_len, cfg.dim, cfg.ffn_dim, cfg.txt_len, cfg.img_len
+    M = batch * L
+    f = {
+        "qkv": 2 * M * D * 3 * D,
+        "self_attention": 4 * batch * L * L * D,
+        "o_proj": 2 * M * D * D,
+        "cross_q": 2 * M * D * D,
+        "ctx_kv": 2 * batch * (Lt + Li) * D * 2 * D,
+        "cross_attention": 4 * batch * L * (Lt + Li) * D,
+        "cross_o": 2 * M * D * D,
+        "ffn1": 2 * M * D * F,
+        "ffn2": 2 * M * F * D,
+    }
+    return f
+
+
+def step_flops(cfg: S.WanConfig) -> float:
+    B2 = 2 * cfg.batch
+    M = B2 * cfg.seq_len
+    per_block = sum(block_flops(cfg, B2).values())
+    patch = 2 * M * cfg.patch_k * cfg.dim
+    head = 2 * M * cfg.dim * 64
+    time_mlp = 2 * (256 * cfg.dim + cfg.dim * cfg.dim + 6 * cfg.dim * cfg.dim)
+    return cfg.n_blocks * per_block + patch + head + time_mlp
+
+
+def cpu_baseline(cfg: S.WanConfig, budget_s: float = 20.0) -> dict:
+    """The float64 oracle on a bounded sample of the same workload: one 1.3B block with the
+    keys/values of all 32760 tokens and the outputs of a sample of query rows."""
+    from oracle import wan_oracle as O
+    bcfg = cfg.with_(n_blocks=1)
+    w = S.block_weights(bcfg, 0)
+    x = S.block_inputs(bcfg)
+    mod = S.modulation(bcfg)
+    ctx = S.context(bcfg, "cond")
+    L, D, F = bcfg.seq_len, bcfg.dim, bcfg.ffn_dim
+    n_rows = 64
+    rows = np.linspace(0, L - 1, n_rows).astype(int).tolist()
+    t0 = time.perf_counter()
+    O.dit_block(x, mod, ctx, w, bcfg.heads, bcfg.grid, bcfg.img_len, rows=rows)
+    dt = time.perf_counter() - t0
+    # algorithmic FLOPs actually performed by the sample
+    n = len(rows)
+    fl = (2 * L * D * 2 * D                      # k, v projections of every token
+          + 2 * n * D * D                        # q of the sampled rows
+          + 4 * n * L * D                        # self-attention of the sampled rows
+          + 2 * n * D * D * 3                    # o, cross q, cross o
+          + 2 * bcfg.txt_len * D * 2 * D         # context k, v
+          + 4 * n * bcfg.txt_len * D             # cross-attention
+          + 4 * n * D * F)                       # FFN
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle, one 1.3B block (L=32760, D=1536): k/v of all tokens, outputs of {n} "
+                      f"query rows; {fl / 1e12:.3f} TFLOP in {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="wan13b_step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the hot path here is one GPU's share of the work "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import video_diffusion_transformer_forward_amd as W
+    from video_diffusion_transformer_forward_amd import _native as N
+
+    cfg = S.get_config(args.config)
+    assert cfg.mode == "bf16"
+    print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
+    mw = S.model_weights(cfg)
+    blocks = [W.DeviceBlock(cfg, S.block_weights(cfg, b)) for b in range(cfg.n_blocks)]
+    model = W.DeviceModel(cfg, mw, blocks)
+    z0 = torch.from_numpy(S.latent(cfg)).cuda()
+    cond = S.condition(cfg)
+    cond = torch.from_numpy(cond).cuda() if cond is not None else None
+    et = W.elem_dtype(cfg)
+    ctx_c = torch.from_numpy(S.context(cfg, "cond")).to(et).cuda()
+    ctx_n = torch.from_numpy(S.context(cfg, "null")).to(et).cuda()
+    ws = W.workspace(cfg, N.ENTRY_STEP)
+    z = z0.clone()
+    torch.cuda.synchronize()
+
+    def step():
+        W.denoise_step(cfg, model, z, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    W.timing_enable(True)
+    for k in range(4):
+        W.timing_read(k, reset=True)
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    W.timing_enable(False)
+    kt = {k: W.timing_read(c) for k, c in (("self_attention", N.KERNEL_SELF_ATTENTION),
+                                           ("cross_attention", N.KERNEL_CROSS_ATTENTION),
+                                           ("gemm", N.KERNEL_GEMM), ("elementwise", N.KERNEL_ELEMENTWISE))}
+    assert bool(torch.isfinite(z).all())
+
+    ms_step = elapsed / args.steps * 1e3
+    flops = step_flops(cfg)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    bf = block_flops(cfg, 2 * cfg.batch)
+    attn_ms, attn_n = kt["self_attention"]
+    attn_avg = attn_ms / max(attn_n, 1)
+    attn_achieved = bf["self_attention"] / (attn_avg * 1e-3) / 1e12
+    per_block_ms = ms_step / cfg.n_blocks
+    block_tflops = sum(bf.values()) / (per_block_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latents/context, N(0,0.02) random-init weights)",
+        "config": {"workload": f"{cfg.name}: one CFG denoise step of the 1.3B DiT, latent 16x{cfg.frames}x"
+                               f"{cfg.height}x{cfg.width} (480p x 81 frames), L={cfg.seq_len}, D={cfg.dim}, "
+                               f"{cfg.heads}x{cfg.head_dim} heads, FFN {cfg.ffn_dim}, {cfg.n_blocks} blocks, "
+                               f"CFG batch 2, {cfg.txt_len} text tokens",
+                   "global_batch": 2 * cfg.batch, "seq_len": cfg.seq_len, "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * tflops / MI355X_BF16_TFLOPS, 2),
+        "ms_per_block_forward_cfg_batch": round(per_block_ms, 3),
+        "block_tflops": round(block_tflops, 2),
+        "step_tflop": round(flops / 1e12, 3),
+        "kernel_ms_per_step": {k: round(v[0] / args.steps, 3) for k, v in kt.items()},
+        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_kernel<bf16,128>)",
+                     "achieved": round(attn_achieved, 2), "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_achieved / MI355X_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(attn_avg, 4), "launches": attn_n,
+                     "flop_per_launch": bf["self_attention"]},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

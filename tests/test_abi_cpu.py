@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point,
+and rejects invalid arguments with the documented codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_diffusion_transformer_forward_amd import _native as N
+from video_diffusion_transformer_forward_amd import shape_of, workspace_bytes
+from video_diffusion_transformer_forward_amd.synth import CONFIGS, TEST_CONFIGS, get_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "wan.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(wan_[a-z_]+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = N.load()
+    names = declared_functions()
+    assert set(names) == set(N.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = N.load()
+    for code in range(0, -8, -1):
+        assert lib.wan_status_str(code)
+    assert b"unknown" in lib.wan_status_str(42)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS) + list(TEST_CONFIGS))
+def test_workspace_sizes(name):
+    cfg = get_config(name)
+    for entry in (N.ENTRY_BLOCK, N.ENTRY_STEP, N.ENTRY_HEAD, N.ENTRY_TIME_EMBED):
+        assert workspace_bytes(cfg, entry) > 0
+    assert workspace_bytes(cfg, N.ENTRY_PATCHIFY) == 0
+    # the step holds a CFG batch of two plus the residual stream: more than one block
+    assert workspace_bytes(cfg, N.ENTRY_STEP) > workspace_bytes(cfg, N.ENTRY_BLOCK)
+
+
+def _ws_status(**kw):
+    lib = N.load()
+    cfg = get_config("toy").with_(**kw)
+    sh = shape_of(cfg)
+    st = ctypes.c_int(99)
+    n = lib.wan_workspace_bytes(ctypes.byref(sh), N.ENTRY_BLOCK, ctypes.byref(st))
+    return st.value, n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(height=15), N.WAN_E_SHAPE), (dict(width=0), N.WAN_E_SHAPE), (dict(heads=3), N.WAN_E_SHAPE),
+    (dict(dim=384, heads=4), N.WAN_E_SHAPE), (dict(heads=2, dim=192), N.WAN_E_SHAPE),
+    (dict(in_ch=20), N.WAN_E_SHAPE), (dict(txt_len=0), N.WAN_E_SHAPE), (dict(ffn_dim=1000), N.WAN_E_SHAPE),
+    (dict(mode="fp32"), N.WAN_OK), (dict(batch=0), N.WAN_E_SHAPE), (dict(img_len=-1), N.WAN_E_SHAPE),
+    (dict(dim=6144, heads=48), N.WAN_E_SHAPE),
+])
+def test_shape_validation(kw, code):
+    st, n = _ws_status(**kw)
+    assert st == code
+    assert (n > 0) == (code == N.WAN_OK)
+
+
+def test_mode_and_entry_validation():
+    lib = N.load()
+    sh = shape_of(get_config("toy"))
+    sh.mode = 7
+    st = ctypes.c_int(0)
+    assert lib.wan_workspace_bytes(ctypes.byref(sh), N.ENTRY_BLOCK, ctypes.byref(st)) == 0
+    assert st.value == N.WAN_E_MODE
+    sh.mode = N.WAN_FP32
+    assert lib.wan_workspace_bytes(ctypes.byref(sh), 99, ctypes.byref(st)) == 0
+    assert st.value == N.WAN_E_ENTRY
+    assert lib.wan_workspace_bytes(None, N.ENTRY_BLOCK, ctypes.byref(st)) == 0
+    assert st.value == N.WAN_E_NULL
+
+
+FAKE = 0x100000  # an aligned address that is never dereferenced: validation fails first or no device is found
+
+
+def _block_call(x=FAKE, mod=FAKE, ctx=FAKE, ws=FAKE, ws_bytes=1 << 40, stride=0, weights=None, cfg="toy"):
+    lib = N.load()
+    sh = shape_of(get_config(cfg))
+    bw = weights or N.WanBlockWeights(*([FAKE] * 16))
+    return lib.wan_dit_block_forward(ctypes.byref(sh), ctypes.byref(bw), x, mod, stride, ctx, ws, ws_bytes, None)
+
+
+def test_block_argument_errors_before_any_hip_call():
+    assert _block_call(x=None) == N.WAN_E_NULL
+    assert _block_call(ctx=None) == N.WAN_E_NULL
+    assert _block_call(x=FAKE + 4) == N.WAN_E_ALIGN
+    assert _block_call(ws=None) == N.WAN_E_WORKSPACE
+    assert _block_call(ws_bytes=1024) == N.WAN_E_WORKSPACE
+    assert _block_call(stride=5) == N.WAN_E_SHAPE
+    w = N.WanBlockWeights(*([FAKE] * 16))
+    w.ff2_w = None
+    assert _block_call(weights=w) == N.WAN_E_NULL
+    # image tokens need their own K/V projection
+    lib = N.load()
+    cfg = get_config("toy_i2v_fp32")
+    sh = shape_of(cfg)
+    w = N.WanBlockWeights(*([FAKE] * 16))
+    w.ikv_w = None
+    assert lib.wan_dit_block_forward(ctypes.byref(sh), ctypes.byref(w), FAKE, FAKE, 0, FAKE, FAKE, 1 << 40,
+                                     None) == N.WAN_E_NULL
+
+
+def test_step_argument_errors():
+    lib = N.load()
+    cfg = get_config("toy_step")
+    sh = shape_of(cfg)
+    blocks = (N.WanBlockWeights * 2)(N.WanBlockWeights(*([FAKE] * 16)), N.WanBlockWeights(*([FAKE] * 16)))
+    mw = N.WanModelWeights(*([FAKE] * 10), 2, ctypes.cast(blocks, ctypes.POINTER(N.WanBlockWeights)))
+    call = lambda **k: lib.wan_denoise_step(ctypes.byref(sh), ctypes.byref(mw), k.get("z", FAKE), None, FAKE, FAKE,
+                                            500.0, k.get("dt", 0.05), 5.0, FAKE, k.get("wsb", 1 << 40), None)
+    assert call(z=None) == N.WAN_E_NULL
+    assert call(dt=float("nan")) == N.WAN_E_SHAPE
+    assert call(wsb=16) == N.WAN_E_WORKSPACE
+    blocks[1].qkv_w = None
+    assert call() == N.WAN_E_NULL
+
+
+def test_no_device_reported_as_hip_error():
+    """With valid arguments the first HIP query fails on a host without a gfx950 GPU."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    assert _block_call() == N.WAN_E_HIP

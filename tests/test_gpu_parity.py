@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Every case prints its name before touching the GPU.  Errors are normwise
+relative errors; the bar is 1e-2 for bf16 operands with float32 accumulation
+and 1e-5 for the float32 mode.  Block results are compared on the increment
+x_out - x_in (the residual dominates x_out itself).
+"""
+import numpy as np
+import pytest
+
+from oracle import wan_oracle as O
+from video_diffusion_transformer_forward_amd import synth as S
+
+from gpu_helpers import (TOL, announce, inc_err, block_case, ctx_dev, device_model, gpu_block, gpu_step, native,
+                         oracle_block, rel_err, sample_rows, to_dev, torch, W)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BLOCK = ["toy", "mid_fp32", "mid_bf16", "mid_i2v_bf16", "mid_b2_bf16", "toy_i2v_fp32"]
+
+
+# ----------------------------------------------------------------------------- patchify
+@pytest.mark.parametrize("name", ["toy", "mid_bf16", "mid_i2v_bf16", "toy_i2v_fp32", "wan13b_block",
+                                  "wan14b_i2v_block"])
+def test_patchify(name):
+    cfg = S.get_config(name)
+    announce(f"patchify {name}")
+    mw = S.model_weights(cfg)
+    z = S.latent(cfg)
+    cond = S.condition(cfg)
+    lib = W()
+    et = lib.elem_dtype(cfg)
+    t = torch()
+    x = t.empty((cfg.batch, cfg.seq_len, cfg.dim), dtype=t.float32, device="cuda")
+    lib.patchify(cfg, to_dev(z), to_dev(cond) if cond is not None else None, to_dev(mw["pe_w"], et),
+                 to_dev(mw["pe_b"]), x)
+    t.cuda.synchronize()
+    got = x.cpu().numpy()
+    # the GPU takes the latent as bf16 operands in bf16 mode; the oracle sees the float32 latent
+    ref = O.patchify(z, cond, mw["pe_w"], mw["pe_b"])
+    err = rel_err(got, ref)
+    print(f"{name}: rel err {err:.3e}")
+    assert err <= TOL[cfg.mode]
+
+
+# ----------------------------------------------------------------------------- time modulation
+@pytest.mark.parametrize("name,tau", [("toy", 500.0), ("toy", 0.0), ("mid_bf16", 999.0), ("wan13b_block", 500.0)])
+def test_time_embed(name, tau):
+    cfg = S.get_config(name)
+    announce(f"time_embed {name} tau={tau}")
+    mw = S.model_weights(cfg)
+    lib = W()
+    t = torch()
+    model = device_model(cfg, mw, [])
+    mod = t.empty((6, cfg.dim), dtype=t.float32, device="cuda")
+    ws = lib.workspace(cfg, native().ENTRY_TIME_EMBED)
+    lib.time_embed(cfg, model, tau, mod, ws)
+    t.cuda.synchronize()
+    ref = O.time_modulation(tau, mw["t1_w"], mw["t1_b"], mw["t2_w"], mw["t2_b"], mw["m_w"], mw["m_b"])
+    err = rel_err(mod.cpu().numpy(), ref)
+    print(f"{name}: rel err {err:.3e}")
+    # weights are exact inputs in both modes; the GEMVs accumulate in float32
+    assert err <= 1e-5
+
+
+# ----------------------------------------------------------------------------- block
+@pytest.mark.parametrize("name", SMALL_BLOCK)
+def test_block_small(name):
+    cfg = S.get_config(name)
+    announce(f"block {name}")
+    w, x, mod, ctx = block_case(cfg)
+    got = gpu_block(cfg, w, x, mod, ctx)
+    ref = oracle_block(cfg, w, x, mod, ctx)
+    err = inc_err(got, ref, x)
+    print(f"{name}: rel err of the increment {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[cfg.mode]
+
+
+@pytest.mark.parametrize("name", ["toy", "mid_bf16"])
+def test_block_shared_modulation(name):
+    """mod given once as (6, D) with batch stride 0."""
+    cfg = S.get_config(name).with_(batch=2)
+    announce(f"block shared-mod {name}")
+    w, x, mod, ctx = block_case(cfg)
+    m1 = mod[0]
+    got = gpu_block(cfg, w, x, m1, ctx, mod_stride=0)
+    ref = oracle_block(cfg, w, x, m1, ctx)
+    assert inc_err(got, ref, x) <= TOL[cfg.mode]
+
+
+@pytest.mark.parametrize("name", ["toy", "mid_bf16"])
+def test_block_sublayer_isolation(name):
+    """Each sublayer alone: the other two switched off through gates / W_co."""
+    cfg = S.get_config(name)
+    w, x, mod, ctx = block_case(cfg)
+    cases = {
+        "self-attention": dict(zero=[5], zero_co=True),
+        "cross-attention": dict(zero=[2, 5], zero_co=False),
+        "ffn": dict(zero=[2], zero_co=True),
+    }
+    for label, c in cases.items():
+        announce(f"block {name} isolation {label}")
+        m = mod.copy()
+        for i in c["zero"]:
+            m[:, i] = 0.0
+        ww = dict(w)
+        if c["zero_co"]:
+            ww["co_w"] = np.zeros_like(w["co_w"])
+            ww["co_b"] = np.zeros_like(w["co_b"])
+        got = gpu_block(cfg, ww, x, m, ctx)
+        ref = oracle_block(cfg, ww, x, m, ctx)
+        err = inc_err(got, ref, x)
+        print(f"{name} {label}: {err:.3e}")
+        assert err <= TOL[cfg.mode], label
+
+
+@pytest.mark.parametrize("name", ["toy", "mid_bf16", "mid_i2v_bf16"])
+def test_block_identity_when_gates_zero(name):
+    cfg = S.get_config(name)
+    announce(f"block identity {name}")
+    w, x, mod, ctx = block_case(cfg, zero_co=True)
+    mod[:, 2] = 0.0
+    mod[:, 5] = 0.0
+    got = gpu_block(cfg, w, x, mod, ctx)
+    np.testing.assert_array_equal(got, x)
+
+
+@pytest.mark.parametrize("name", ["mid_bf16", "mid_fp32"])
+def test_block_attention_stress(name):
+    """Peaked softmax: q/k weights scaled so the logits have std ~4, and b_v = 0."""
+    base = S.get_config(name)
+    cfg = base.with_(qk_std=float(np.sqrt(4.0 / base.dim)))
+    announce(f"block stress {name}")
+    w, x, mod, ctx = block_case(cfg)
+    w["qkv_b"][2 * cfg.dim:] = 0.0      # b_v = 0: the output is all weighting
+    m = mod.copy()
+    m[:, 5] = 0.0
+    w["co_w"] = np.zeros_like(w["co_w"])
+    w["co_b"] = np.zeros_like(w["co_b"])
+    got = gpu_block(cfg, w, x, m, ctx)
+    ref = oracle_block(cfg, w, x, m, ctx)
+    err = inc_err(got, ref, x)
+    print(f"{name} stress: {err:.3e}")
+    assert err <= TOL[cfg.mode]
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_block_degenerate_single_token(mode):
+    """L = 1 token, one text token: every tile is a ragged tail."""
+    cfg = S.WanConfig("tiny", 21, frames=1, height=2, width=2, dim=256, heads=2, ffn_dim=256, txt_len=1,
+                      mode=mode)
+    announce(f"block single token {mode}")
+    w, x, mod, ctx = block_case(cfg)
+    got = gpu_block(cfg, w, x, mod, ctx)
+    ref = oracle_block(cfg, w, x, mod, ctx)
+    assert inc_err(got, ref, x) <= TOL[mode]
+
+
+def test_block_deterministic():
+    cfg = S.get_config("mid_bf16")
+    announce("block determinism")
+    w, x, mod, ctx = block_case(cfg)
+    a = gpu_block(cfg, w, x, mod, ctx)
+    b = gpu_block(cfg, w, x, mod, ctx)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_block_wan13b_full_size_sampled_rows():
+    """The 1.3B block at 480p x 81 frames (L = 32760): sampled token rows against the oracle."""
+    cfg = S.get_config("wan13b_block")
+    announce("block wan13b full size")
+    w, x, mod, ctx = block_case(cfg)
+    got = gpu_block(cfg, w, x, mod, ctx)
+    assert np.all(np.isfinite(got))
+    rows = sample_rows(cfg.seq_len, 48, seed=3)
+    ref = oracle_block(cfg, w, x, mod, ctx, rows=rows)
+    err = inc_err(got[:, rows], ref, x[:, rows])
+    print(f"wan13b sampled rows: rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- head
+@pytest.mark.parametrize("name", ["toy", "mid_bf16"])
+def test_head(name):
+    cfg = S.get_config(name)
+    announce(f"head {name}")
+    mw = S.model_weights(cfg)
+    x = S.block_inputs(cfg)
+    lib = W()
+    t = torch()
+    model = device_model(cfg, mw, [])
+    v = t.empty((cfg.batch, 16, cfg.frames, cfg.height, cfg.width), dtype=t.float32, device="cuda")
+    ws = lib.workspace(cfg, native().ENTRY_HEAD)
+    lib.head(cfg, model, to_dev(x), v, ws)
+    t.cuda.synchronize()
+    ref = O.patch_scatter(O.head(x, mw["hd_w"], mw["hd_b"]), cfg.frames, cfg.height, cfg.width)
+    err = rel_err(v.cpu().numpy(), ref)
+    print(f"{name}: {err:.3e}")
+    assert err <= TOL[cfg.mode]
+
+
+# ----------------------------------------------------------------------------- denoise step
+@pytest.mark.parametrize("name", ["toy_step", "mid_step_bf16"])
+def test_step_small(name):
+    cfg = S.get_config(name)
+    announce(f"step {name}")
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    z = S.latent(cfg)
+    cond = S.condition(cfg)
+    cc, cn = S.context(cfg, "cond"), S.context(cfg, "null")
+    got = gpu_step(cfg, mw, bw, z, cond, cc, cn, cfg.timestep, cfg.dt, cfg.guide_scale)
+    ref = O.denoise_step(z, cond, cc, cn, mw, bw, cfg.heads, cfg.timestep, cfg.dt, cfg.guide_scale, cfg.img_len)
+    err = inc_err(got, ref, z)
+    print(f"{name}: rel err of dt*v {err:.3e}")
+    assert err <= TOL[cfg.mode]
+
+
+def test_step_i2v_small():
+    cfg = S.get_config("toy_i2v_fp32").with_(n_blocks=2)
+    announce("step toy_i2v_fp32")
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    z, cond = S.latent(cfg), S.condition(cfg)
+    cc, cn = S.context(cfg, "cond"), S.context(cfg, "null")
+    got = gpu_step(cfg, mw, bw, z, cond, cc, cn, 250.0, 0.05, 5.0)
+    ref = O.denoise_step(z, cond, cc, cn, mw, bw, cfg.heads, 250.0, 0.05, 5.0, cfg.img_len)
+    assert inc_err(got, ref, z) <= TOL["fp32"]
+
+
+def test_step_wan13b_one_block_sampled():
+    """The 1.3B step shape (CFG batch 2, L = 32760) with one block: sampled tokens against the oracle."""
+    cfg = S.get_config("wan13b_step").with_(n_blocks=1)
+    announce("step wan13b one block")
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, 0)]
+    z = S.latent(cfg)
+    cc, cn = S.context(cfg, "cond"), S.context(cfg, "null")
+    got = gpu_step(cfg, mw, bw, z, None, cc, cn, cfg.timestep, cfg.dt, cfg.guide_scale)
+    rows = sample_rows(cfg.seq_len, 24, seed=5)
+    x = O.patchify(z, None, mw["pe_w"], mw["pe_b"])
+    mod = O.time_modulation(cfg.timestep, mw["t1_w"], mw["t1_b"], mw["t2_w"], mw["t2_b"], mw["m_w"], mw["m_b"])
+    v = []
+    for ctx in (cc, cn):
+        xr = O.dit_block(x, mod, ctx, bw[0], cfg.heads, cfg.grid, 0, rows=rows)
+        v.append(O.head(xr, mw["hd_w"], mw["hd_b"]))       # (1, n, 64)
+    vv = O.cfg_combine(v[0], v[1], cfg.guide_scale)[0]
+    F, Hh, Ww = cfg.grid
+    g_out, r_out, z_in = [], [], []
+    for n, l in enumerate(rows):
+        f, rem = divmod(l, Hh * Ww)
+        i, j = divmod(rem, Ww)
+        for c in range(16):
+            for a in range(2):
+                for b in range(2):
+                    zv = float(z[0, c, f, 2 * i + a, 2 * j + b])
+                    z_in.append(zv)
+                    g_out.append(got[0, c, f, 2 * i + a, 2 * j + b])
+                    r_out.append(zv + cfg.dt * vv[n, c * 4 + a * 2 + b])
+    err = inc_err(g_out, r_out, z_in)
+    print(f"wan13b step one block sampled: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_step_wan13b_30_blocks_properties():
+    """Full 30-block 1.3B step: guidance linearity and identity blocks, at full size."""
+    cfg = S.get_config("wan13b_step")
+    announce("step wan13b 30 blocks properties")
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    z = S.latent(cfg)
+    cc, cn = S.context(cfg, "cond"), S.context(cfg, "null")
+    model = device_model(cfg, mw, bw)
+    zs = {g: gpu_step(cfg, mw, bw, z, None, cc, cn, cfg.timestep, cfg.dt, g, model=model) for g in (0.0, 1.0, 5.0)}
+    for g in zs.values():
+        assert np.all(np.isfinite(g))
+    d1 = zs[1.0].astype(np.float64) - zs[0.0]
+    d5 = zs[5.0].astype(np.float64) - zs[0.0]
+    err = rel_err(d5, 5 * d1)
+    print(f"guidance linearity: {err:.3e}")
+    assert err <= 1e-3
+    # identity blocks: both gates and the cross-attention output projection zero
+    mw0 = dict(mw)
+    D = cfg.dim
+    mw0["m_w"] = mw["m_w"].copy()
+    mw0["m_b"] = mw["m_b"].copy()
+    for r in (2, 5):
+        mw0["m_w"][r * D:(r + 1) * D] = 0.0
+        mw0["m_b"][r * D:(r + 1) * D] = 0.0
+    bw0 = []
+    for b in bw:
+        b0 = dict(b)
+        b0["co_w"] = np.zeros_like(b["co_w"])
+        b0["co_b"] = np.zeros_like(b["co_b"])
+        bw0.append(b0)
+    del model
+    got = gpu_step(cfg, mw0, bw0, z, None, cc, cn, cfg.timestep, cfg.dt, cfg.guide_scale)
+    v = O.patch_scatter(O.head(O.patchify(z, None, mw["pe_w"], mw["pe_b"]), mw["hd_w"], mw["hd_b"]),
+                        cfg.frames, cfg.height, cfg.width)
+    err = inc_err(got, z + cfg.dt * v, z)
+    print(f"identity-block step: {err:.3e}")
+    assert err <= TOL["bf16"]

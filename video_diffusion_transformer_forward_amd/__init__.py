@@ -1,0 +1,149 @@
+"""Wan2.1 DiT block and CFG/Euler denoise step on MI355X (gfx950).
+
+Thin torch-facing binding of libwan.so (include/wan.h): every function below
+only marshals tensor pointers, shapes and the current HIP stream into the C ABI.
+All computation runs in the library's HIP kernels; there is no other path.
+PyTorch provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _native as N
+from ._native import WanError  # noqa: F401
+from .synth import WanConfig
+
+__all__ = ["shape_of", "DeviceBlock", "DeviceModel", "workspace", "workspace_bytes", "patchify", "time_embed",
+           "dit_block_forward", "head", "denoise_step", "timing_enable", "timing_read", "WanError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def elem_dtype(cfg: WanConfig):
+    torch = _torch()
+    return torch.bfloat16 if cfg.mode == "bf16" else torch.float32
+
+
+def shape_of(cfg: WanConfig) -> N.WanShape:
+    return N.WanShape(cfg.batch, cfg.in_ch, cfg.out_ch, cfg.frames, cfg.height, cfg.width, cfg.dim, cfg.heads,
+                      cfg.ffn_dim, cfg.txt_len, cfg.img_len, N.WAN_BF16 if cfg.mode == "bf16" else N.WAN_FP32)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_bytes(cfg: WanConfig, entry: int) -> int:
+    lib = N.load()
+    st = ctypes.c_int(0)
+    sh = shape_of(cfg)
+    n = lib.wan_workspace_bytes(ctypes.byref(sh), entry, ctypes.byref(st))
+    N.check(st.value)
+    return int(n)
+
+
+def workspace(cfg: WanConfig, entry: int, device="cuda"):
+    torch = _torch()
+    n = workspace_bytes(cfg, entry)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _dev(a, dtype, device):
+    torch = _torch()
+    return torch.as_tensor(a).to(device=device, dtype=dtype).contiguous()
+
+
+class DeviceBlock:
+    """One block's weights resident on the device, plus the ABI struct pointing at them."""
+
+    def __init__(self, cfg: WanConfig, w: dict, device="cuda"):
+        torch = _torch()
+        et = elem_dtype(cfg)
+        self.t = {k: _dev(v, torch.float32 if k.endswith("_b") else et, device) for k, v in w.items()}
+        f = {k: _ptr(v) for k, v in self.t.items()}
+        self.struct = N.WanBlockWeights(*[f.get(n) for n, _ in N.WanBlockWeights._fields_])
+
+
+class DeviceModel:
+    """Model-level weights (patch embedding, time MLP, head) and a list of DeviceBlock."""
+
+    def __init__(self, cfg: WanConfig, mw: dict, blocks=(), device="cuda"):
+        torch = _torch()
+        et = elem_dtype(cfg)
+        self.t = {k: _dev(v, torch.float32 if k.endswith("_b") else et, device) for k, v in mw.items()}
+        self.blocks = list(blocks)
+        self._arr = (N.WanBlockWeights * max(1, len(self.blocks)))(*[b.struct for b in self.blocks])
+        f = {k: _ptr(v) for k, v in self.t.items()}
+        vals = [f.get(n) for n, _ in N.WanModelWeights._fields_[:10]]
+        self.struct = N.WanModelWeights(*vals, len(self.blocks),
+                                        ctypes.cast(self._arr, ctypes.POINTER(N.WanBlockWeights)))
+
+
+def patchify(cfg, z, cond, pe_w, pe_b, x, stream=None):
+    """wan_patchify: x (B, L, D) float32 <- (1,2,2) patch embedding of [z ; cond]."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    N.check(lib.wan_patchify(ctypes.byref(sh), _ptr(z), _ptr(cond), _ptr(pe_w), _ptr(pe_b), _ptr(x), None, 0,
+                             _stream(stream)))
+    return x
+
+
+def time_embed(cfg, model: DeviceModel, timestep: float, mod, ws, stream=None):
+    """wan_time_embed: mod (6, D) float32 from the timestep."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    N.check(lib.wan_time_embed(ctypes.byref(sh), ctypes.byref(model.struct), float(timestep), _ptr(mod), _ptr(ws),
+                               ws.numel(), _stream(stream)))
+    return mod
+
+
+def dit_block_forward(cfg, block: DeviceBlock, x, mod, ctx, ws, mod_batch_stride=None, stream=None):
+    """wan_dit_block_forward: one block in place on x (B, L, D) float32."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    if mod_batch_stride is None:
+        mod_batch_stride = 6 * cfg.dim if mod.dim() == 3 else 0
+    N.check(lib.wan_dit_block_forward(ctypes.byref(sh), ctypes.byref(block.struct), _ptr(x), _ptr(mod),
+                                      int(mod_batch_stride), _ptr(ctx), _ptr(ws), ws.numel(), _stream(stream)))
+    return x
+
+
+def head(cfg, model: DeviceModel, x, v, ws, stream=None):
+    """wan_head: v (B, 16, F, H, W) float32 from the residual stream x."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    N.check(lib.wan_head(ctypes.byref(sh), ctypes.byref(model.struct), _ptr(x), _ptr(v), _ptr(ws), ws.numel(),
+                         _stream(stream)))
+    return v
+
+
+def timing_enable(on: bool = True):
+    """Bracket library kernel launches with HIP events (measurement only)."""
+    N.check(N.load().wan_timing_enable(1 if on else 0))
+
+
+def timing_read(kernel_class: int, reset: bool = True):
+    """(total ms, launches) of one kernel class since the last reset; waits for its events."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_longlong(0)
+    N.check(N.load().wan_timing_read(kernel_class, ctypes.byref(ms), ctypes.byref(n), 1 if reset else 0))
+    return ms.value, n.value
+
+
+def denoise_step(cfg, model: DeviceModel, z, cond, ctx_cond, ctx_null, timestep, dt, guide_scale, ws, stream=None):
+    """wan_denoise_step: one CFG + Euler step in place on z (B, 16, F, H, W) float32."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    N.check(lib.wan_denoise_step(ctypes.byref(sh), ctypes.byref(model.struct), _ptr(z), _ptr(cond), _ptr(ctx_cond),
+                                 _ptr(ctx_null), float(timestep), float(dt), float(guide_scale), _ptr(ws),
+                                 ws.numel(), _stream(stream)))
+    return z

@@ -1,0 +1,578 @@
+// C ABI: argument validation, workspace planning and the launch sequences of
+// the patchify, time-modulation, block, head and denoise-step entry points.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/wan.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace wan {
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_DIM = 5120;  // the LayerNorm kernel keeps one row in a wave's registers
+constexpr int MAX_CTX = 65536;
+constexpr int MAX_TOKENS = 1 << 20;
+constexpr int TIME_DIM = 256;
+
+size_t al(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+int pad64(int x) { return (x + 63) / 64 * 64; }
+
+struct Dims {
+  int B, Cin, F, H, W, Hh, Ww, L, Lp, D, heads, hd, Ff, Lt, Li, Lc, Ltp, Lip, mode;
+  size_t es;
+};
+
+int check_shape(const wan_shape* s, Dims* d) {
+  if (!s) return WAN_E_NULL;
+  if (s->mode != WAN_BF16 && s->mode != WAN_FP32) return WAN_E_MODE;
+  if (s->batch < 1 || (s->in_ch != 16 && s->in_ch != 36) || s->out_ch != 16) return WAN_E_SHAPE;
+  if (s->frames < 1 || s->height < 2 || s->width < 2 || (s->height & 1) || (s->width & 1)) return WAN_E_SHAPE;
+  if (s->dim < 256 || s->dim % 256 != 0 || s->dim > MAX_DIM) return WAN_E_SHAPE;
+  if (s->heads < 1 || s->dim % s->heads != 0) return WAN_E_SHAPE;
+  const int hd = s->dim / s->heads;
+  if (hd != 64 && hd != 128) return WAN_E_SHAPE;
+  if (s->ffn_dim < 256 || s->ffn_dim % 256 != 0 || s->ffn_dim > (1 << 16)) return WAN_E_SHAPE;
+  if (s->txt_len < 1 || s->img_len < 0 || s->txt_len + s->img_len > MAX_CTX) return WAN_E_SHAPE;
+  const long long L = (long long)s->frames * (s->height / 2) * (s->width / 2);
+  if (L > MAX_TOKENS || (long long)s->batch * L * 2 > (1LL << 30)) return WAN_E_SHAPE;
+  if (s->batch > 64) return WAN_E_SHAPE;
+  if (d) {
+    d->B = s->batch;
+    d->Cin = s->in_ch;
+    d->F = s->frames;
+    d->H = s->height;
+    d->W = s->width;
+    d->Hh = s->height / 2;
+    d->Ww = s->width / 2;
+    d->L = (int)L;
+    d->Lp = pad64((int)L);
+    d->D = s->dim;
+    d->heads = s->heads;
+    d->hd = hd;
+    d->Ff = s->ffn_dim;
+    d->Lt = s->txt_len;
+    d->Li = s->img_len;
+    d->Lc = s->txt_len + s->img_len;
+    d->Ltp = pad64(s->txt_len);
+    d->Lip = pad64(s->img_len);
+    d->mode = s->mode;
+    d->es = s->mode == WAN_BF16 ? 2 : 4;
+  }
+  return WAN_OK;
+}
+
+// Offsets (bytes) inside the workspace of one block run over Bb batch rows.
+struct BlockPlan {
+  size_t m, r1, q, k, vt, o, ck, cvt, ik, ivt, rope, total;
+};
+
+size_t rope_entries(const Dims& d) {
+  const int ds = 2 * (d.hd / 6), df = d.hd - 2 * ds;
+  return (size_t)d.F * (df / 2) + (size_t)d.Hh * (ds / 2) + (size_t)d.Ww * (ds / 2);
+}
+
+BlockPlan plan_block(const Dims& d, int Bb, size_t base) {
+  BlockPlan p;
+  const size_t es = d.es;
+  size_t off = base;
+  p.m = off;
+  off += al((size_t)Bb * d.L * d.D * es);
+  const size_t qkv1 = al((size_t)Bb * d.heads * d.Lp * d.hd * es);
+  const size_t hbytes = al((size_t)Bb * d.L * d.Ff * es);
+  p.r1 = off;
+  p.q = off;
+  p.k = off + qkv1;
+  p.vt = off + 2 * qkv1;
+  off += (3 * qkv1 > hbytes ? 3 * qkv1 : hbytes);
+  p.o = off;
+  off += al((size_t)Bb * d.L * d.D * es);
+  p.ck = off;
+  off += al((size_t)Bb * d.heads * d.Ltp * d.hd * es);
+  p.cvt = off;
+  off += al((size_t)Bb * d.heads * d.Ltp * d.hd * es);
+  p.ik = off;
+  p.ivt = off;
+  if (d.Li > 0) {
+    off += al((size_t)Bb * d.heads * d.Lip * d.hd * es);
+    p.ivt = off;
+    off += al((size_t)Bb * d.heads * d.Lip * d.hd * es);
+  }
+  p.rope = off;
+  off += al(rope_entries(d) * sizeof(float2));
+  p.total = off;
+  return p;
+}
+
+struct StepPlan {
+  size_t x, mod, t1, t2, p, ctx;
+  BlockPlan blk;
+  size_t total;
+};
+
+StepPlan plan_step(const Dims& d) {
+  StepPlan p;
+  size_t off = 0;
+  const int B2 = 2 * d.B;
+  p.x = off;
+  off += al((size_t)B2 * d.L * d.D * 4);
+  p.mod = off;
+  off += al((size_t)6 * d.D * 4);
+  p.t1 = off;
+  off += al((size_t)d.D * 4);
+  p.t2 = off;
+  off += al((size_t)d.D * 4);
+  p.p = off;
+  off += al((size_t)B2 * d.L * 64 * 4);
+  p.ctx = off;
+  off += al((size_t)B2 * d.Lc * d.D * d.es);
+  p.blk = plan_block(d, B2, off);
+  p.total = p.blk.total;
+  return p;
+}
+
+size_t head_bytes(const Dims& d) { return al((size_t)d.B * d.L * d.D * d.es) + al((size_t)d.B * d.L * 64 * 4); }
+size_t time_bytes(const Dims& d) { return 2 * al((size_t)d.D * 4); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (!p) return WAN_E_NULL;
+    if (!aligned16(p)) return WAN_E_ALIGN;
+  }
+  return WAN_OK;
+}
+
+int check_block_weights(const wan_block_weights* w, const Dims& d) {
+  if (!w) return WAN_E_NULL;
+  int rc = check_ptrs({w->qkv_w, w->qkv_b, w->o_w, w->o_b, w->cq_w, w->cq_b, w->ckv_w, w->ckv_b, w->co_w, w->co_b,
+                       w->ff1_w, w->ff1_b, w->ff2_w, w->ff2_b});
+  if (rc) return rc;
+  if (d.Li > 0) return check_ptrs({w->ikv_w, w->ikv_b});
+  return WAN_OK;
+}
+
+int check_model_weights(const wan_model_weights* w, const Dims& d, bool blocks) {
+  if (!w) return WAN_E_NULL;
+  int rc = check_ptrs({w->pe_w, w->pe_b, w->t1_w, w->t1_b, w->t2_w, w->t2_b, w->m_w, w->m_b, w->hd_w, w->hd_b});
+  if (rc) return rc;
+  if (blocks) {
+    if (w->n_blocks < 0 || w->n_blocks > 1024) return WAN_E_SHAPE;
+    if (w->n_blocks > 0 && !w->blocks) return WAN_E_NULL;
+    for (int i = 0; i < w->n_blocks; ++i) {
+      rc = check_block_weights(&w->blocks[i], d);
+      if (rc) return rc;
+    }
+  }
+  return WAN_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return WAN_OK;
+  if (!ws || ws_bytes < need) return WAN_E_WORKSPACE;
+  if (!aligned16(ws)) return WAN_E_ALIGN;
+  return WAN_OK;
+}
+
+// A gfx950 device must be current; the answer is cached per device.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return WAN_E_HIP;
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 ok, -1 unusable
+  if (dev >= 64) return WAN_E_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return WAN_E_HIP;
+    known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return known[dev] == 1 ? WAN_OK : WAN_E_HIP;
+}
+
+#define HIP_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return WAN_E_HIP; \
+  } while (0)
+
+// ---- optional event timing of kernel classes
+constexpr int N_CLASSES = 4;
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;                                // free events
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[N_CLASSES];
+  double ms[N_CLASSES] = {0, 0, 0, 0};
+  long long n[N_CLASSES] = {0, 0, 0, 0};
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+hipEvent_t take_event(Timing& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Run `launch` (returning hipError_t), bracketed by events when timing is on.
+template <typename F>
+hipError_t timed(int cls, hipStream_t st, F&& launch) {
+  Timing& t = timing();
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(t.mu);
+    if (t.on) {
+      a = take_event(t);
+      b = take_event(t);
+    }
+  }
+  if (a && b) {
+    if (hipEventRecord(a, st) != hipSuccess) return hipErrorUnknown;
+  }
+  hipError_t e = launch();
+  if (a && b) {
+    if (hipEventRecord(b, st) != hipSuccess) return hipErrorUnknown;
+    std::lock_guard<std::mutex> lock(t.mu);
+    t.pending[cls].emplace_back(a, b);
+  }
+  return e;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+template <typename T>
+int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const float* mod, long long mbs,
+              const void* ctx, void* ws, const BlockPlan& p, bool rope_ready, hipStream_t st) {
+  const int M = Bb * d.L;
+  T* m = reinterpret_cast<T*>(at(ws, p.m));
+  T* o = reinterpret_cast<T*>(at(ws, p.o));
+  float2* rope = reinterpret_cast<float2*>(at(ws, p.rope));
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.hd));
+
+  if (!rope_ready) HIP_TRY(launch_rope_table(rope, d.hd, d.F, d.Hh, d.Ww, st));
+
+  // self-attention sublayer
+  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, mod + 0 * d.D, mod + 1 * d.D, mbs, st); }));
+  HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.vt), Bb * d.heads, d.hd, d.L, d.Lp, st));
+  {
+    GemmArgs g;
+    g.M = M; g.N = 3 * d.D; g.K = d.D;
+    g.A = m; g.lda = d.D; g.a_rpb = M; g.a_bstride = 0;
+    g.Wt = w->qkv_w; g.ldw = d.D; g.bias = w->qkv_b;
+    g.c_rpb = d.L;
+    g.q = at(ws, p.q); g.k = at(ws, p.k); g.vt = at(ws, p.vt);
+    g.nq = d.D; g.nk = d.D; g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
+    g.rope = rope; g.gF = d.F; g.gH = d.Hh; g.gW = d.Ww;
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
+  }
+  {
+    AttnArgs a;
+    a.q = at(ws, p.q); a.Lq = d.L; a.Lqp = d.Lp;
+    a.k[0] = at(ws, p.k); a.vt[0] = at(ws, p.vt); a.Lk[0] = d.L; a.Lkp[0] = d.Lp; a.nsrc = 1;
+    a.o = o; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
+    HIP_TRY(timed(WAN_KERNEL_SELF_ATTENTION, st, [&] { return launch_attention<T>(a, st); }));
+  }
+  {
+    GemmArgs g;
+    g.M = M; g.N = d.D; g.K = d.D;
+    g.A = o; g.lda = d.D; g.a_rpb = M;
+    g.Wt = w->o_w; g.ldw = d.D; g.bias = w->o_b;
+    g.c_rpb = d.L; g.x = x; g.ldx = d.D; g.gate = mod + 2 * d.D; g.gate_bstride = mbs;
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_RESID, st); }));
+  }
+
+  // cross-attention sublayer (ungated)
+  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, nullptr, nullptr, 0, st); }));
+  {
+    GemmArgs g;
+    g.M = M; g.N = d.D; g.K = d.D;
+    g.A = m; g.lda = d.D; g.a_rpb = M;
+    g.Wt = w->cq_w; g.ldw = d.D; g.bias = w->cq_b;
+    g.c_rpb = d.L; g.q = at(ws, p.q); g.nq = d.D; g.nk = 0;
+    g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
+  }
+  {
+    GemmArgs g;
+    g.M = Bb * d.Lt; g.N = 2 * d.D; g.K = d.D;
+    g.A = static_cast<const char*>(ctx) + (size_t)d.Li * d.D * d.es;
+    g.lda = d.D; g.a_rpb = d.Lt; g.a_bstride = (long long)d.Lc * d.D;
+    g.Wt = w->ckv_w; g.ldw = d.D; g.bias = w->ckv_b;
+    g.c_rpb = d.Lt; g.k = at(ws, p.ck); g.vt = at(ws, p.cvt); g.nq = 0; g.nk = d.D;
+    g.heads = d.heads; g.hd = d.hd; g.Lp = d.Ltp;
+    HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.cvt), Bb * d.heads, d.hd, d.Lt, d.Ltp, st));
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
+  }
+  if (d.Li > 0) {
+    GemmArgs g;
+    g.M = Bb * d.Li; g.N = 2 * d.D; g.K = d.D;
+    g.A = ctx; g.lda = d.D; g.a_rpb = d.Li; g.a_bstride = (long long)d.Lc * d.D;
+    g.Wt = w->ikv_w; g.ldw = d.D; g.bias = w->ikv_b;
+    g.c_rpb = d.Li; g.k = at(ws, p.ik); g.vt = at(ws, p.ivt); g.nq = 0; g.nk = d.D;
+    g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lip;
+    HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.ivt), Bb * d.heads, d.hd, d.Li, d.Lip, st));
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
+  }
+  {
+    AttnArgs a;
+    a.q = at(ws, p.q); a.Lq = d.L; a.Lqp = d.Lp;
+    a.k[0] = at(ws, p.ck); a.vt[0] = at(ws, p.cvt); a.Lk[0] = d.Lt; a.Lkp[0] = d.Ltp;
+    a.nsrc = 1;
+    if (d.Li > 0) {
+      a.k[1] = at(ws, p.ik); a.vt[1] = at(ws, p.ivt); a.Lk[1] = d.Li; a.Lkp[1] = d.Lip; a.nsrc = 2;
+    }
+    a.o = o; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
+    HIP_TRY(timed(WAN_KERNEL_CROSS_ATTENTION, st, [&] { return launch_attention<T>(a, st); }));
+  }
+  {
+    GemmArgs g;
+    g.M = M; g.N = d.D; g.K = d.D;
+    g.A = o; g.lda = d.D; g.a_rpb = M;
+    g.Wt = w->co_w; g.ldw = d.D; g.bias = w->co_b;
+    g.c_rpb = d.L; g.x = x; g.ldx = d.D; g.gate = nullptr;
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_RESID, st); }));
+  }
+
+  // FFN sublayer
+  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, mod + 3 * d.D, mod + 4 * d.D, mbs, st); }));
+  T* hbuf = reinterpret_cast<T*>(at(ws, p.r1));
+  {
+    GemmArgs g;
+    g.M = M; g.N = d.Ff; g.K = d.D;
+    g.A = m; g.lda = d.D; g.a_rpb = M;
+    g.Wt = w->ff1_w; g.ldw = d.D; g.bias = w->ff1_b;
+    g.c_rpb = d.L; g.C = hbuf; g.ldc = d.Ff;
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_STORE_GELU, st); }));
+  }
+  {
+    GemmArgs g;
+    g.M = M; g.N = d.D; g.K = d.Ff;
+    g.A = hbuf; g.lda = d.Ff; g.a_rpb = M;
+    g.Wt = w->ff2_w; g.ldw = d.Ff; g.bias = w->ff2_b;
+    g.c_rpb = d.L; g.x = x; g.ldx = d.D; g.gate = mod + 5 * d.D; g.gate_bstride = mbs;
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_RESID, st); }));
+  }
+  return WAN_OK;
+}
+
+template <typename T>
+int run_patchify(const Dims& d, int Bout, const float* z, const float* cond, const void* pe_w, const float* pe_b,
+                 float* x, hipStream_t st) {
+  GemmArgs g;
+  g.M = Bout * d.L; g.N = d.D; g.K = d.Cin * 4;
+  g.z = z; g.cond = cond; g.z_batch = d.B; g.in_ch = d.Cin; g.F = d.F; g.H = d.H; g.W = d.W;
+  g.Wt = pe_w; g.ldw = d.Cin * 4; g.bias = pe_b;
+  g.c_rpb = d.L; g.C = x; g.ldc = d.D;
+  HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PATCH, EPI_STORE_F32, st); }));
+  return WAN_OK;
+}
+
+template <typename T>
+int run_time(const Dims& d, const wan_model_weights* w, float tau, float* mod, float* t1, float* t2, hipStream_t st) {
+  HIP_TRY(launch_gemv<T>(w->t1_w, w->t1_b, nullptr, tau, t1, d.D, TIME_DIM, 0, st));
+  HIP_TRY(launch_gemv<T>(w->t2_w, w->t2_b, t1, 0.f, t2, d.D, d.D, 1, st));
+  HIP_TRY(launch_gemv<T>(w->m_w, w->m_b, t2, 0.f, mod, 6 * d.D, d.D, 1, st));
+  return WAN_OK;
+}
+
+template <typename T>
+int run_head(const Dims& d, int Bb, const wan_model_weights* w, const float* x, void* mbuf, float* p, hipStream_t st) {
+  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, mbuf, Bb * d.L, d.D, d.L, nullptr, nullptr, 0, st); }));
+  GemmArgs g;
+  g.M = Bb * d.L; g.N = 64; g.K = d.D;
+  g.A = mbuf; g.lda = d.D; g.a_rpb = g.M;
+  g.Wt = w->hd_w; g.ldw = d.D; g.bias = w->hd_b;
+  g.c_rpb = d.L; g.C = p; g.ldc = 64;
+  HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_STORE_F32, st); }));
+  return WAN_OK;
+}
+
+}  // namespace
+}  // namespace wan
+
+using namespace wan;
+
+extern "C" {
+
+const char* wan_status_str(int code) {
+  switch (code) {
+    case WAN_OK: return "ok";
+    case WAN_E_NULL: return "a required pointer is NULL";
+    case WAN_E_SHAPE: return "unsupported or inconsistent shape";
+    case WAN_E_MODE: return "unknown precision mode";
+    case WAN_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case WAN_E_WORKSPACE: return "workspace missing or too small";
+    case WAN_E_HIP: return "no usable gfx950 device, or a HIP launch failed";
+    case WAN_E_ENTRY: return "unknown entry id";
+  }
+  return "unknown status code";
+}
+
+size_t wan_workspace_bytes(const wan_shape* s, int entry, int* status) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  size_t n = 0;
+  if (rc == WAN_OK) {
+    switch (entry) {
+      case WAN_ENTRY_PATCHIFY: n = 0; break;
+      case WAN_ENTRY_BLOCK: n = plan_block(d, d.B, 0).total; break;
+      case WAN_ENTRY_STEP: n = plan_step(d).total; break;
+      case WAN_ENTRY_TIME_EMBED: n = time_bytes(d); break;
+      case WAN_ENTRY_HEAD: n = head_bytes(d); break;
+      default: rc = WAN_E_ENTRY;
+    }
+  }
+  if (status) *status = rc;
+  return rc == WAN_OK ? n : 0;
+}
+
+int wan_patchify(const wan_shape* s, const float* z, const float* cond, const void* pe_w, const float* pe_b,
+                 float* x, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if ((rc = check_ptrs({z, pe_w, pe_b, x}))) return rc;
+  if (d.Cin == 36 && (rc = check_ptrs({cond}))) return rc;
+  (void)ws;
+  (void)ws_bytes;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return d.mode == WAN_BF16 ? run_patchify<bf16>(d, d.B, z, d.Cin == 36 ? cond : nullptr, pe_w, pe_b, x, st)
+                            : run_patchify<float>(d, d.B, z, d.Cin == 36 ? cond : nullptr, pe_w, pe_b, x, st);
+}
+
+int wan_time_embed(const wan_shape* s, const wan_model_weights* w, float timestep, float* mod, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if ((rc = check_model_weights(w, d, false))) return rc;
+  if ((rc = check_ptrs({mod}))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, time_bytes(d)))) return rc;
+  if (!isfinite(timestep)) return WAN_E_SHAPE;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* t1 = reinterpret_cast<float*>(at(ws, 0));
+  float* t2 = reinterpret_cast<float*>(at(ws, al((size_t)d.D * 4)));
+  return d.mode == WAN_BF16 ? run_time<bf16>(d, w, timestep, mod, t1, t2, st)
+                            : run_time<float>(d, w, timestep, mod, t1, t2, st);
+}
+
+int wan_dit_block_forward(const wan_shape* s, const wan_block_weights* w, float* x, const float* mod,
+                          long long mod_batch_stride, const void* ctx, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if ((rc = check_block_weights(w, d))) return rc;
+  if ((rc = check_ptrs({x, mod, ctx}))) return rc;
+  if (mod_batch_stride != 0 && mod_batch_stride != 6LL * d.D) return WAN_E_SHAPE;
+  const BlockPlan p = plan_block(d, d.B, 0);
+  if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return d.mode == WAN_BF16 ? run_block<bf16>(d, d.B, w, x, mod, mod_batch_stride, ctx, ws, p, false, st)
+                            : run_block<float>(d, d.B, w, x, mod, mod_batch_stride, ctx, ws, p, false, st);
+}
+
+int wan_head(const wan_shape* s, const wan_model_weights* w, const float* x, float* v, void* ws, size_t ws_bytes,
+             void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if ((rc = check_model_weights(w, d, false))) return rc;
+  if ((rc = check_ptrs({x, v}))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, head_bytes(d)))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* mbuf = at(ws, 0);
+  float* p = reinterpret_cast<float*>(at(ws, al((size_t)d.B * d.L * d.D * d.es)));
+  rc = d.mode == WAN_BF16 ? run_head<bf16>(d, d.B, w, x, mbuf, p, st) : run_head<float>(d, d.B, w, x, mbuf, p, st);
+  if (rc) return rc;
+  HIP_TRY(launch_unpatch(p, v, d.B, 16, d.F, d.H, d.W, 0, 0.f, 0.f, st));
+  return WAN_OK;
+}
+
+int wan_denoise_step(const wan_shape* s, const wan_model_weights* w, float* z, const float* cond,
+                     const void* ctx_cond, const void* ctx_null, float timestep, float dt, float guide_scale,
+                     void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if ((rc = check_model_weights(w, d, true))) return rc;
+  if ((rc = check_ptrs({z, ctx_cond, ctx_null}))) return rc;
+  if (d.Cin == 36 && (rc = check_ptrs({cond}))) return rc;
+  if (!isfinite(timestep) || !isfinite(dt) || !isfinite(guide_scale)) return WAN_E_SHAPE;
+  const StepPlan p = plan_step(d);
+  if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int B2 = 2 * d.B;
+  float* x = reinterpret_cast<float*>(at(ws, p.x));
+  float* mod = reinterpret_cast<float*>(at(ws, p.mod));
+  float* pbuf = reinterpret_cast<float*>(at(ws, p.p));
+  void* ctx2 = at(ws, p.ctx);
+  const size_t ctx_bytes = (size_t)d.B * d.Lc * d.D * d.es;
+  HIP_TRY(copy_async(ctx2, ctx_cond, ctx_bytes, st));
+  HIP_TRY(copy_async(static_cast<char*>(ctx2) + ctx_bytes, ctx_null, ctx_bytes, st));
+  const float* cnd = d.Cin == 36 ? cond : nullptr;
+  if (d.mode == WAN_BF16) {
+    if ((rc = run_time<bf16>(d, w, timestep, mod, (float*)at(ws, p.t1), (float*)at(ws, p.t2), st))) return rc;
+    if ((rc = run_patchify<bf16>(d, B2, z, cnd, w->pe_w, w->pe_b, x, st))) return rc;
+    for (int i = 0; i < w->n_blocks; ++i)
+      if ((rc = run_block<bf16>(d, B2, &w->blocks[i], x, mod, 0, ctx2, ws, p.blk, i > 0, st))) return rc;
+    if ((rc = run_head<bf16>(d, B2, w, x, at(ws, p.blk.m), pbuf, st))) return rc;
+  } else {
+    if ((rc = run_time<float>(d, w, timestep, mod, (float*)at(ws, p.t1), (float*)at(ws, p.t2), st))) return rc;
+    if ((rc = run_patchify<float>(d, B2, z, cnd, w->pe_w, w->pe_b, x, st))) return rc;
+    for (int i = 0; i < w->n_blocks; ++i)
+      if ((rc = run_block<float>(d, B2, &w->blocks[i], x, mod, 0, ctx2, ws, p.blk, i > 0, st))) return rc;
+    if ((rc = run_head<float>(d, B2, w, x, at(ws, p.blk.m), pbuf, st))) return rc;
+  }
+  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_unpatch(pbuf, z, d.B, 16, d.F, d.H, d.W, 1, dt, guide_scale, st); }));
+  return WAN_OK;
+}
+
+int wan_timing_enable(int on) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.on = on != 0;
+  return WAN_OK;
+}
+
+int wan_timing_read(int kernel_class, double* ms_total, long long* launches, int reset) {
+  if (kernel_class < 0 || kernel_class >= N_CLASSES) return WAN_E_ENTRY;
+  if (!ms_total || !launches) return WAN_E_NULL;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  for (auto& pr : t.pending[kernel_class]) {
+    if (hipEventSynchronize(pr.second) != hipSuccess) return WAN_E_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return WAN_E_HIP;
+    t.ms[kernel_class] += ms;
+    t.n[kernel_class] += 1;
+    t.pool.push_back(pr.first);
+    t.pool.push_back(pr.second);
+  }
+  t.pending[kernel_class].clear();
+  *ms_total = t.ms[kernel_class];
+  *launches = t.n[kernel_class];
+  if (reset) {
+    t.ms[kernel_class] = 0;
+    t.n[kernel_class] = 0;
+  }
+  return WAN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device-side helpers shared by the gfx950 kernels: element types, 8-element
+// operand chunks and the 32x32 MFMA step used by the GEMM and attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wan {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// An operand chunk: 8 consecutive elements along the contraction axis, the
+// per-lane operand of one 32x32x16 MFMA step.  bf16: 16 bytes, float: 32 bytes.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Chunks are moved with explicit vector loads and stores only (never struct
+// assignment), so they stay in registers.
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> {
+  u32x4 v;
+  __device__ __forceinline__ void zero() { v = (u32x4){0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void store(void* p) const { *reinterpret_cast<u32x4*>(p) = v; }
+};
+template <> struct Chunk<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void zero() {
+    a = (f32x4){0.f, 0.f, 0.f, 0.f};
+    b = a;
+  }
+  __device__ __forceinline__ void load(const void* p) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    a = q[0];
+    b = q[1];
+  }
+  __device__ __forceinline__ void store(void* p) const {
+    f32x4* q = reinterpret_cast<f32x4*>(p);
+    q[0] = a;
+    q[1] = b;
+  }
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// acc(32x32) += A(32x16) * B(16x32).  Lane l supplies A[l%32][8*(l/32) + e] and
+// B[8*(l/32) + e][l%32] for e < 8; acc element r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32.  For float operands the same k-chunk
+// is contracted by eight 32x32x2 steps, step e taking element e of each lane's
+// chunk, so both element types share one operand layout.
+__device__ __forceinline__ void mma32(f32x16& acc, const Chunk<bf16>& a, const Chunk<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a.v), as_bf16x8(b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& acc, const Chunk<float>& a, const Chunk<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[e], b.a[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[e], b.b[e], acc, 0, 0, 0);
+}
+
+// float -> bf16 with round-to-nearest-even (gfx950 converts in hardware).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+__device__ __forceinline__ float bf16_to_f(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return to_bf16(x); }
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<bf16>(bf16 x) { return bf16_to_f(x); }
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+
+// Pack 8 floats into a chunk of T.
+__device__ __forceinline__ void pack8(Chunk<bf16>& c, const float* f) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = to_bf16(f[e]);
+  c.v = __builtin_bit_cast(u32x4, v);
+}
+__device__ __forceinline__ void pack8(Chunk<float>& c, const float* f) {
+  c.a = (f32x4){f[0], f[1], f[2], f[3]};
+  c.b = (f32x4){f[4], f[5], f[6], f[7]};
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+__device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
+
+// Workgroups are handed to the 8 XCDs round-robin; this maps the hardware
+// order so that each XCD receives one contiguous range of logical ids.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  const int nx = 8;
+  int full = n - n % nx;
+  if (id >= full) return id;
+  return (id % nx) * (full / nx) + id / nx;
+}
+
+}  // namespace wan

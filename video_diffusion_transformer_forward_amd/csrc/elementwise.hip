@@ -1,0 +1,243 @@
+// Bandwidth-bound kernels: fused LayerNorm + AdaLN modulation, the RoPE
+// cos/sin table, the time-embedding GEMVs, v^T key-padding fill, and the fused
+// unpatchify + classifier-free guidance + Euler update.
+#include "common.h"
+#include "kernels.h"
+
+namespace wan {
+
+namespace {
+
+constexpr int LN_MAX_V4 = 20;  // up to D = 5120 per wave (20 float4 per lane)
+
+// One wave per row: the row stays in registers between the mean, the variance
+// and the output pass (two-pass statistics, biased variance, eps 1e-6).
+template <typename T>
+__global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, T* __restrict__ out, int rows,
+                                                     int D, int rows_per_batch, const float* __restrict__ shift,
+                                                     const float* __restrict__ scale, long long mod_bstride) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nv = D / 256;  // float4 per lane
+  const float4* xr = reinterpret_cast<const float4*>(x + (long long)row * D);
+  float4 v[LN_MAX_V4];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < LN_MAX_V4; ++i) {
+    if (i < nv) {
+      v[i] = xr[i * 64 + lane];
+      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float mean = wave_sum(s) / D;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < LN_MAX_V4; ++i) {
+    if (i < nv) {
+      float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+  }
+  const float var = wave_sum(q) / D;
+  const float rstd = 1.0f / sqrtf(var + 1e-6f);
+  const int b = row / rows_per_batch;
+  const float* sh = shift ? shift + (long long)b * mod_bstride : nullptr;
+  const float* sc = scale ? scale + (long long)b * mod_bstride : nullptr;
+  T* orow = out + (long long)row * D;
+#pragma unroll
+  for (int i = 0; i < LN_MAX_V4; ++i) {
+    if (i < nv) {
+      const int col = (i * 64 + lane) * 4;
+      float r[4] = {(v[i].x - mean) * rstd, (v[i].y - mean) * rstd, (v[i].z - mean) * rstd,
+                    (v[i].w - mean) * rstd};
+      if (sc) {
+        const float4 s4 = *reinterpret_cast<const float4*>(sc + col);
+        const float4 h4 = *reinterpret_cast<const float4*>(sh + col);
+        r[0] = r[0] * (1.f + s4.x) + h4.x;
+        r[1] = r[1] * (1.f + s4.y) + h4.y;
+        r[2] = r[2] * (1.f + s4.z) + h4.z;
+        r[3] = r[3] * (1.f + s4.w) + h4.w;
+      }
+      if (sizeof(T) == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 o4;
+        o4[0] = to_bf16(r[0]);
+        o4[1] = to_bf16(r[1]);
+        o4[2] = to_bf16(r[2]);
+        o4[3] = to_bf16(r[3]);
+        *reinterpret_cast<bf16x4*>(orow + col) = o4;
+      } else {
+        *reinterpret_cast<float4*>(orow + col) = make_float4(r[0], r[1], r[2], r[3]);
+      }
+    }
+  }
+}
+
+// (cos, sin) of pos * 10000^(-2r/d_axis) for the three axes, in double.
+__global__ void rope_table_kernel(float2* tab, int hd, int F, int Hh, int Ww) {
+  const int ds = 2 * (hd / 6);
+  const int df = hd - 2 * ds;
+  const int n0 = F * (df / 2), n1 = Hh * (ds / 2), n2 = Ww * (ds / 2);
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n0 + n1 + n2) return;
+  int pos, r, da;
+  if (idx < n0) {
+    pos = idx / (df / 2);
+    r = idx % (df / 2);
+    da = df;
+  } else if (idx < n0 + n1) {
+    pos = (idx - n0) / (ds / 2);
+    r = (idx - n0) % (ds / 2);
+    da = ds;
+  } else {
+    pos = (idx - n0 - n1) / (ds / 2);
+    r = (idx - n0 - n1) % (ds / 2);
+    da = ds;
+  }
+  const double theta = pow(10000.0, -2.0 * r / (double)da);
+  const double phi = pos * theta;
+  tab[idx] = make_float2((float)cos(phi), (float)sin(phi));
+}
+
+__device__ __forceinline__ int vt_perm_e(int t) { return (t & ~0xC) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2); }
+
+template <typename T>
+__global__ void zero_vt_pad_kernel(T* vt, int rows, int L, int Lp) {
+  const int pad = Lp - L;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)rows * pad) return;
+  const long long row = idx / pad;
+  const int t = L + (int)(idx - row * pad);
+  vt[row * Lp + vt_perm_e(t)] = from_f<T>(0.f);
+}
+
+// One wave per output: y[n] = sum_k W[n][k] act(x[k]) + b[n].  The input
+// vector (K <= 8192) is staged once per workgroup in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ Wt, const float* __restrict__ bias,
+                                                   const float* __restrict__ x, float tau, float* __restrict__ y,
+                                                   int N, int K, int silu_in) {
+  __shared__ float xs[8192];
+  for (int k = threadIdx.x; k < K; k += 256) {
+    float v;
+    if (x) {
+      v = x[k];
+    } else {
+      // timestep sinusoid: [cos(tau w_i) ; sin(tau w_i)], w_i = 10000^(-i/half)
+      const int half = K / 2;
+      const int i = k < half ? k : k - half;
+      const double w = pow(10000.0, -(double)i / half);
+      const double arg = (double)tau * w;
+      v = (float)(k < half ? cos(arg) : sin(arg));
+    }
+    xs[k] = silu_in ? silu(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const T* wr = Wt + (long long)n * K;
+  float acc = 0.f;
+  for (int k = lane * 8; k < K; k += 64 * 8) {
+    Chunk<T> c;
+    c.load(wr + k);
+    const T* e = reinterpret_cast<const T*>(&c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += to_f<T>(e[u]) * xs[k + u];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) y[n] = acc + (bias ? bias[n] : 0.f);
+}
+
+// out[b][c][f][y][x] from the head rows p[(b, token)][c*4 + (y%2)*2 + x%2].
+// step: out holds z; z += dt * (p_null + g (p_cond - p_null)), p_null = rows of batch B + b.
+__global__ void unpatch_kernel(const float* __restrict__ p, float* __restrict__ out, int B, int C, int F, int H,
+                               int W, int step, float dt, float guide) {
+  const long long n = (long long)B * C * F * H * W;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  long long r = idx;
+  const int xw = (int)(r % W); r /= W;
+  const int yh = (int)(r % H); r /= H;
+  const int f = (int)(r % F); r /= F;
+  const int c = (int)(r % C); r /= C;
+  const int b = (int)r;
+  const int Hh = H / 2, Ww = W / 2;
+  const long long L = (long long)F * Hh * Ww;
+  const long long tok = ((long long)f * Hh + yh / 2) * Ww + xw / 2;
+  const int k = c * 4 + (yh & 1) * 2 + (xw & 1);
+  const int K = C * 4;
+  const float pc = p[((long long)b * L + tok) * K + k];
+  if (!step) {
+    out[idx] = pc;
+  } else {
+    const float pu = p[((long long)(B + b) * L + tok) * K + k];
+    const float v = pu + guide * (pc - pu);
+    out[idx] = out[idx] + dt * v;
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_ln_mod(const float* x, void* out, int rows, int D, int rows_per_batch, const float* shift,
+                         const float* scale, long long mod_bstride, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (D % 256 != 0 || D / 256 > LN_MAX_V4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ln_mod_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, x, reinterpret_cast<T*>(out), rows,
+                     D, rows_per_batch, shift, scale, mod_bstride);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2* tab, int hd, int F, int Hh, int Ww, hipStream_t st) {
+  const int ds = 2 * (hd / 6);
+  const int df = hd - 2 * ds;
+  const int n = F * (df / 2) + Hh * (ds / 2) + Ww * (ds / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, tab, hd, F, Hh, Ww);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_zero_vt_pad(void* vt, int BH, int hd, int L, int Lp, hipStream_t st) {
+  const long long n = (long long)BH * hd * (Lp - L);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_vt_pad_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<T*>(vt), BH * hd, L, Lp);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gemv(const void* Wt, const float* bias, const float* x, float tau, float* y, int N, int K,
+                       int silu_in, hipStream_t st) {
+  if (K > 8192 || K % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemv_kernel<T>, dim3((N + 3) / 4), dim3(256), 0, st, reinterpret_cast<const T*>(Wt), bias, x,
+                     tau, y, N, K, silu_in);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpatch(const float* p, float* out, int B, int C, int F, int H, int W, int step, float dt,
+                          float guide, hipStream_t st) {
+  const long long n = (long long)B * C * F * H * W;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(unpatch_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, out, B, C, F, H, W,
+                     step, dt, guide);
+  return hipGetLastError();
+}
+
+hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+}
+
+template hipError_t launch_ln_mod<bf16>(const float*, void*, int, int, int, const float*, const float*, long long,
+                                        hipStream_t);
+template hipError_t launch_ln_mod<float>(const float*, void*, int, int, int, const float*, const float*, long long,
+                                         hipStream_t);
+template hipError_t launch_zero_vt_pad<bf16>(void*, int, int, int, int, hipStream_t);
+template hipError_t launch_zero_vt_pad<float>(void*, int, int, int, int, hipStream_t);
+template hipError_t launch_gemv<bf16>(const void*, const float*, const float*, float, float*, int, int, int,
+                                      hipStream_t);
+template hipError_t launch_gemv<float>(const void*, const float*, const float*, float, float*, int, int, int,
+                                       hipStream_t);
+
+}  // namespace wan

@@ -1,0 +1,92 @@
+// Internal launchers of the gfx950 kernels (host side).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wan {
+
+enum Loader { LOAD_PLAIN = 0, LOAD_PATCH = 1 };
+enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_STORE_F32 = 2, EPI_RESID = 3, EPI_PACK = 4 };
+
+// C[M][N] = A[M][K] * W[N][K]^T + bias, with an epilogue selected by `epi`.
+struct GemmArgs {
+  int M = 0, N = 0, K = 0;
+  // A operand (LOAD_PLAIN): row r lives at A + (r / a_rpb) * a_bstride + (r % a_rpb) * lda
+  const void* A = nullptr;
+  long long lda = 0, a_bstride = 0;
+  int a_rpb = 1;
+  // A operand (LOAD_PATCH): (1,2,2) patches of [z ; cond], token rows of `zb_count` videos
+  const float* z = nullptr;
+  const float* cond = nullptr;
+  int z_batch = 1;          // videos held by z / cond (row batch b reads video b % z_batch)
+  int in_ch = 16, F = 1, H = 2, W = 2;
+  // weights
+  const void* Wt = nullptr;
+  long long ldw = 0;
+  const float* bias = nullptr;
+  // rows of C belong to batch b = r / c_rpb, token t = r % c_rpb
+  int c_rpb = 1;
+  // EPI_STORE*: C + r * ldc + n
+  void* C = nullptr;
+  long long ldc = 0;
+  // EPI_RESID: x[r * ldx + n] += gate[b * gate_bstride + n] * (acc + bias); gate NULL -> 1
+  float* x = nullptr;
+  long long ldx = 0;
+  const float* gate = nullptr;
+  long long gate_bstride = 0;
+  // EPI_PACK: columns [0, nq) -> q, [nq, nq+nk) -> k, rest -> v^T; all head-major
+  void* q = nullptr;
+  void* k = nullptr;
+  void* vt = nullptr;
+  int nq = 0, nk = 0;
+  int heads = 1, hd = 128, Lp = 64;
+  const float2* rope = nullptr;  // (cos, sin) table or NULL for no rotation
+  int gF = 1, gH = 1, gW = 1;    // RoPE grid (frames, rows, cols)
+};
+
+template <typename T> hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st);
+
+// Flash attention over head-major q [B][H][Lqp][hd], k [B][H][Lkp][hd],
+// v^T [B][H][hd][Lkp] (keys permuted inside each 16-key group), one or two
+// key/value sources summed after their own softmax.  Output o (B, Lq, H*hd).
+struct AttnArgs {
+  const void* q = nullptr;
+  int Lq = 0, Lqp = 0;
+  const void* k[2] = {nullptr, nullptr};
+  const void* vt[2] = {nullptr, nullptr};
+  int Lk[2] = {0, 0}, Lkp[2] = {0, 0};
+  int nsrc = 1;
+  void* o = nullptr;
+  int B = 1, heads = 1, hd = 128;
+  float scale_log2 = 0.f;
+};
+template <typename T> hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+// out[r] = T( LN(x[r]) * (1 + scale[b]) + shift[b] ), rows of length D; shift/scale NULL -> plain LN
+template <typename T>
+hipError_t launch_ln_mod(const float* x, void* out, int rows, int D, int rows_per_batch, const float* shift,
+                         const float* scale, long long mod_bstride, hipStream_t st);
+
+// (cos, sin) RoPE table for head dim hd over grid (F, Hh, Ww), computed in double.
+hipError_t launch_rope_table(float2* tab, int hd, int F, int Hh, int Ww, hipStream_t st);
+
+// zero the key padding [L, Lp) of a v^T buffer [BH][hd][Lp]
+template <typename T> hipError_t launch_zero_vt_pad(void* vt, int BH, int hd, int L, int Lp, hipStream_t st);
+
+// y[n] = sum_k W[n][k] * act(x[k]) + b[n]; act = SiLU when silu_in, x float32 of length K.
+// When x is NULL the input is the 256-wide timestep sinusoid of `tau` (computed in double).
+template <typename T>
+hipError_t launch_gemv(const void* Wt, const float* bias, const float* x, float tau, float* y, int N, int K,
+                       int silu_in, hipStream_t st);
+
+// Unpatchify the head output p (rows of out_ch*4) and either store it (dt == 0 && !step)
+// or apply guidance + Euler to z.  Branch layout: p rows [0, B*L) conditional,
+// [B*L, 2*B*L) null when `step`.
+hipError_t launch_unpatch(const float* p, float* out, int B, int C, int F, int H, int W, int step, float dt,
+                          float guide, hipStream_t st);
+
+// copy helper (device to device, on the stream)
+hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t st);
+
+}  // namespace wan
