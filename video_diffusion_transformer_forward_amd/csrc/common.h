@@ -90,7 +90,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+// erf by the rational approximation 7.1.26 of Abramowitz & Stegun's Handbook of
+// Mathematical Functions, |error| < 1.5e-7:
+//   erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),  t = 1 / (1 + p x),  x >= 0
+__device__ __forceinline__ float erf_as26(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, ax, 1.0f));
+  float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  poly = __builtin_fmaf(poly, t, 1.421413741f);
+  poly = __builtin_fmaf(poly, t, -0.284496736f);
+  poly = __builtin_fmaf(poly, t, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(__builtin_fmaf(-poly * t, e, 1.0f), x);
+}
+// GELU(u) = u/2 (1 + erf(u / sqrt 2))
+__device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + erf_as26(u * 0.70710678118654752f)); }
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
 
 // Workgroups are handed to the 8 XCDs round-robin; this maps the hardware

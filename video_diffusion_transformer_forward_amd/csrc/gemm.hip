@@ -1,12 +1,16 @@
 // LDS-tiled MFMA GEMM for gfx950: C = A W^T + bias with fused epilogues.
 //
-// 256 threads (4 waves) per workgroup, a BM x BN tile, BK-deep k-steps, two
-// LDS stages.  Global loads of step k+1 are issued before the MFMAs of step k
-// and written to the idle LDS stage afterwards, one barrier per step.  LDS rows
-// hold 8-element chunks XOR-swizzled by row so that the 32 rows one MFMA
-// operand reads land on distinct banks.  Tiles are ordered in groups of 8
-// M-tiles and the hardware workgroup order is remapped so that each XCD (with
-// its own L2) works on one contiguous group of tiles.
+// 256 threads (4 waves) per workgroup compute a BM x BN tile in BK-deep
+// k-tiles.  Operand tiles stream global -> LDS through the 16-byte LDS-DMA
+// path into an NST-stage ring, so the loads of a k-tile are issued NST-1 tiles
+// ahead of its MFMAs; one barrier per k-tile.  Inside a k-tile the MFMA operand
+// fragments are double-buffered in registers, so the LDS reads of one 16-deep
+// k-step overlap the MFMAs of the previous one.  Tile rows are 64 bytes: four
+// 16-byte chunks whose position is XOR-swizzled with row bits 2..3, which puts
+// the 16 rows one wave-wide operand read touches on distinct banks.  Tiles are
+// ordered in groups of 8 M-tiles and the hardware workgroup order is remapped
+// so that each XCD (with its own L2) works through one contiguous range.
+// The epilogue stages the fp32 tile in LDS and writes 16-byte pieces.
 #include "common.h"
 #include "kernels.h"
 
@@ -14,16 +18,22 @@ namespace wan {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
 struct Gemm {
-  static constexpr int BK = sizeof(T) == 2 ? 64 : 32;
-  static constexpr int CPR = BK / 8;  // chunks per tile row
+  static constexpr int BK = sizeof(T) == 2 ? 32 : 16;  // 64-byte tile rows
+  static constexpr int CPR = BK / 8;                   // chunks per tile row (4 bf16, 2 float)
+  static constexpr int NST = 4;                        // LDS ring stages
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
-  static constexpr int A_PT = BM * CPR / 256;
-  static constexpr int B_PT = BN * CPR / 256;
   static constexpr int STAGE = (BM + BN) * CPR;  // chunks per stage
-  static constexpr size_t PIPE_BYTES = 2 * STAGE * sizeof(Chunk<T>);
+  static constexpr size_t PIPE_BYTES = (size_t)NST * STAGE * sizeof(Chunk<T>);
+  // DMA instructions per wave per k-tile: each covers 16 rows of 64 bytes
+  static constexpr int NA = BM / 64, NB = BN / 64;
+  // register-staged (gathered) path: chunks per thread per k-tile
+  static constexpr int A_PT = (BM * CPR + 255) / 256;
+  static constexpr int B_PT = (BN * CPR + 255) / 256;
   // epilogue slab: the whole tile when it fits the pipeline's LDS, else one wave column
   static constexpr int SW = ((size_t)BM * (BN + 4) * 4 <= PIPE_BYTES) ? BN : BN / WN;
   static constexpr int SWP = SW + 4;
@@ -33,8 +43,15 @@ struct Gemm {
   static_assert(BN % SW == 0 && SW % 8 == 0, "slab");
   static_assert(WM * WN == 4, "4 waves");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
-  static_assert((BM * CPR) % 256 == 0 && (BN * CPR) % 256 == 0, "load split");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA split");
+  static_assert(CPR * sizeof(Chunk<T>) == 64, "64-byte rows");
 };
+
+// physical chunk position of logical chunk c in tile row r
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  return c ^ ((r >> 2) & (CPR - 1));
+}
 
 // Load the 8 patch features [k0, k0+8) of token row (b, t): two channels x (2x2).
 template <typename T>
@@ -66,10 +83,30 @@ __device__ __forceinline__ int vt_perm(int t) {
   return (t & ~0xC) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8]); a field at its maximum does not wait.  Issued through the
+// builtin so that the compiler's own wait insertion accounts for them.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that waits for this wave's LDS reads only.  __syncthreads()
+// would also drain every outstanding global load (vmcnt(0)), i.e. the k-tiles
+// prefetched into the ring; the vmcnt wait for the tile needed next is explicit.
+// The empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   using C = Gemm<T, BM, BN, WM, WN, LOADER, EPI>;
-  constexpr int BK = C::BK, CPR = C::CPR, TM = C::TM, TN = C::TN;
+  constexpr int BK = C::BK, CPR = C::CPR, TM = C::TM, TN = C::TN, NST = C::NST;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Chunk<T>* smem = reinterpret_cast<Chunk<T>*>(smem_raw);
 
@@ -84,86 +121,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   const int nn = g.N / BN;
   const int ntiles = nm * nn;
   const int lid = xcd_remap(blockIdx.x, ntiles);
-  constexpr int GM = 8;
-  const int group = lid / (GM * nn);
-  const int first_m = group * GM;
-  const int gsize = min(nm - first_m, GM);
-  const int in_group = lid - group * GM * nn;
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
+  int tm, tn;
+  if (nn <= 8) {
+    // few N-tiles: all of them run side by side on one XCD, so every A row panel
+    // is fetched from HBM once while each N-tile consumes it
+    tm = lid / nn;
+    tn = lid - tm * nn;
+  } else {
+    constexpr int GM = 8;
+    const int group = lid / (GM * nn);
+    const int first_m = group * GM;
+    const int gsize = min(nm - first_m, GM);
+    const int in_group = lid - group * GM * nn;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+  }
   const int m0 = tm * BM;
   const int n0 = tn * BN;
-
-  // ---- per-thread load rows (fixed across k-steps)
-  const T* a_ptr[C::A_PT];
-  int pf[C::A_PT], pi[C::A_PT], pj[C::A_PT], pzb[C::A_PT];
-#pragma unroll
-  for (int u = 0; u < C::A_PT; ++u) {
-    int idx = tid + 256 * u;
-    int r = m0 + idx / CPR;
-    r = min(r, g.M - 1);
-    if (LOADER == LOAD_PLAIN) {
-      int b = r / g.a_rpb, t = r - b * g.a_rpb;
-      a_ptr[u] = reinterpret_cast<const T*>(g.A) + (long long)b * g.a_bstride + (long long)t * g.lda;
-    } else {
-      int b = r / g.c_rpb, t = r - b * g.c_rpb;
-      int hh = g.H / 2, ww = g.W / 2;
-      pf[u] = t / (hh * ww);
-      int rem = t - pf[u] * hh * ww;
-      pi[u] = rem / ww;
-      pj[u] = rem - pi[u] * ww;
-      pzb[u] = b % g.z_batch;
-    }
-  }
-  const T* b_ptr[C::B_PT];
-#pragma unroll
-  for (int u = 0; u < C::B_PT; ++u) {
-    int idx = tid + 256 * u;
-    b_ptr[u] = reinterpret_cast<const T*>(g.Wt) + (long long)(n0 + idx / CPR) * g.ldw;
-  }
-
-  Chunk<T> ra[C::A_PT], rb[C::B_PT];
-  auto load_tile = [&](int kt) {
-    const int kb = kt * BK;
-#pragma unroll
-    for (int u = 0; u < C::A_PT; ++u) {
-      int c = (tid + 256 * u) % CPR;
-      int k0 = kb + c * 8;
-      if (k0 < g.K) {
-        if (LOADER == LOAD_PLAIN)
-          ra[u].load(a_ptr[u] + k0);
-        else
-          load_patch_chunk<T>(ra[u], g, pzb[u], pf[u], pi[u], pj[u], k0);
-      } else {
-        ra[u].zero();
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < C::B_PT; ++u) {
-      int c = (tid + 256 * u) % CPR;
-      int k0 = kb + c * 8;
-      if (k0 < g.K)
-        rb[u].load(b_ptr[u] + k0);
-      else
-        rb[u].zero();
-    }
-  };
-  auto store_tile = [&](int stage) {
-    Chunk<T>* sa = smem + stage * C::STAGE;
-    Chunk<T>* sb = sa + BM * CPR;
-#pragma unroll
-    for (int u = 0; u < C::A_PT; ++u) {
-      int idx = tid + 256 * u;
-      int r = idx / CPR, c = idx % CPR;
-      ra[u].store(&sa[r * CPR + (c ^ (r & (CPR - 1)))]);
-    }
-#pragma unroll
-    for (int u = 0; u < C::B_PT; ++u) {
-      int idx = tid + 256 * u;
-      int r = idx / CPR, c = idx % CPR;
-      rb[u].store(&sb[r * CPR + (c ^ (r & (CPR - 1)))]);
-    }
-  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -176,59 +150,213 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * (BM / WM);
   const int brow0 = wn * (BN / WN);
-
   const int nk = (g.K + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-    const Chunk<T>* sa = smem + cur * C::STAGE;
+  constexpr int KS = BK / 16;
+
+  // MFMA operand fragments of one 16-deep k step, double-buffered
+  Chunk<T> fa[2][TM], fb[2][TN];
+  auto load_frags = [&](int stage, int ks, int buf) {
+    const Chunk<T>* sa = smem + stage * C::STAGE;
     const Chunk<T>* sb = sa + BM * CPR;
+    const int c = 2 * ks + g2;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = 2 * ks + g2;
-      Chunk<T> fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        int r = arow0 + 32 * i + l32;
-        fa[i].load(&sa[r * CPR + (c ^ (r & (CPR - 1)))]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int r = brow0 + 32 * j + l32;
-        fb[j].load(&sb[r * CPR + (c ^ (r & (CPR - 1)))]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) mma32(acc[i][j], fa[i], fb[j]);
+    for (int i = 0; i < TM; ++i) {
+      const int r = arow0 + 32 * i + l32;
+      fa[buf][i].load(&sa[r * CPR + swz<CPR>(r, c)]);
     }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = brow0 + 32 * j + l32;
+      fb[buf][j].load(&sb[r * CPR + swz<CPR>(r, c)]);
+    }
+  };
+  auto mma_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) mma32(acc[i][j], fb[buf][j], fa[buf][i]);
+  };
+
+  if constexpr (LOADER == LOAD_PLAIN) {
+    // ---- LDS-DMA ring.  One wave instruction fills 1 KB = 16 rows of 64 bytes;
+    // lane l writes the l-th 16 bytes, so the chunk swizzle is applied to the
+    // global address each lane reads.
+    constexpr int SPC = (int)sizeof(Chunk<T>) / 16;
+    constexpr int NA = C::NA, NB = C::NB, DPT = NA + NB;
+    const int pp = lane & 3;          // 16-byte piece within the 64-byte row
+    const int rlow = lane >> 2;       // row within the instruction's 16 rows
+    const int col_off = swz<CPR>(rlow, pp / SPC) * 8 + (pp % SPC) * (8 / SPC);
+    const T* a_src[NA];
+    const T* b_src[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      int r = m0 + (wave * NA + i) * 16 + rlow;
+      r = min(r, g.M - 1);
+      const int bb = r / g.a_rpb, t = r - bb * g.a_rpb;
+      a_src[i] = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda + col_off;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = n0 + (wave * NB + i) * 16 + rlow;
+      b_src[i] = reinterpret_cast<const T*>(g.Wt) + (long long)r * g.ldw + col_off;
+    }
+    auto issue = [&](int kt) {
+      unsigned char* base = smem_raw + (size_t)(kt % NST) * C::STAGE * sizeof(Chunk<T>);
+      const int koff = kt * BK;
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        __builtin_amdgcn_global_load_lds(a_src[i] + koff, (lds_void*)(base + (size_t)(wave * NA + i) * 1024), 16,
+                                         0, 0);
+      unsigned char* bbase = base + (size_t)BM * CPR * sizeof(Chunk<T>);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        __builtin_amdgcn_global_load_lds(b_src[i] + koff, (lds_void*)(bbase + (size_t)(wave * NB + i) * 1024), 16,
+                                         0, 0);
+    };
+    static_assert(NST == 4 && (KS == 1 || KS == 2), "ring of 4, one or two k steps per tile");
+    // Every iteration issues one k-tile (the index clamped at the end, the
+    // redundant copies landing in stages nobody reads again), so exactly two
+    // tiles may stay in flight when the next one is needed.
+    auto issue_c = [&](int kt) { issue(min(kt, nk - 1)); };
+    // the LDS reads of the next fragments interleaved with the MFMAs of this step
+    auto interleave = [&]() {
+#pragma unroll
+      for (int q = 0; q < TM + TN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN) / (TM + TN), 0);  // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      }
+    };
+
+#pragma unroll
+    for (int s0 = 0; s0 < NST - 1; ++s0) issue_c(s0);
+    wait_vmcnt<2 * DPT>();
+    barrier_lds();
+    load_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt % NST;
+      if constexpr (KS == 2) {
+        load_frags(cur, 1, 1);
+        mma_step(0);
+        interleave();
+        // refill the stage of k-tile kt-1 (its last reads preceded the previous barrier)
+        issue_c(kt + NST - 1);
+        wait_vmcnt<2 * DPT>();  // k-tile kt+1 has landed
+        barrier_lds();
+        load_frags((kt + 1) % NST, 0, 0);
+        mma_step(1);
+        interleave();
+      } else {
+        issue_c(kt + NST - 1);
+        mma_step(0);
+        wait_vmcnt<2 * DPT>();
+        barrier_lds();
+        load_frags((kt + 1) % NST, 0, 0);
+      }
+    }
+    wait_vmcnt<0>();
     __syncthreads();
+  } else {
+    // ---- gathered A (patch embedding): global -> registers -> LDS, zero-filled K tail,
+    // two ring stages
+    int pf[C::A_PT], pi[C::A_PT], pj[C::A_PT], pzb[C::A_PT];
+#pragma unroll
+    for (int u = 0; u < C::A_PT; ++u) {
+      int idx = min(tid + 256 * u, BM * CPR - 1);
+      int r = m0 + idx / CPR;
+      r = min(r, g.M - 1);
+      int b = r / g.c_rpb, t = r - b * g.c_rpb;
+      int hh = g.H / 2, ww = g.W / 2;
+      pf[u] = t / (hh * ww);
+      int rem = t - pf[u] * hh * ww;
+      pi[u] = rem / ww;
+      pj[u] = rem - pi[u] * ww;
+      pzb[u] = b % g.z_batch;
+    }
+    const T* b_ptr[C::B_PT];
+#pragma unroll
+    for (int u = 0; u < C::B_PT; ++u) {
+      int idx = min(tid + 256 * u, BN * CPR - 1);
+      b_ptr[u] = reinterpret_cast<const T*>(g.Wt) + (long long)(n0 + idx / CPR) * g.ldw;
+    }
+    Chunk<T> ra[C::A_PT], rb[C::B_PT];
+    auto load_tile = [&](int kt) {
+      const int kb = kt * BK;
+#pragma unroll
+      for (int u = 0; u < C::A_PT; ++u) {
+        int c = (tid + 256 * u) % CPR;
+        int k0 = kb + c * 8;
+        if (k0 < g.K)
+          load_patch_chunk<T>(ra[u], g, pzb[u], pf[u], pi[u], pj[u], k0);
+        else
+          ra[u].zero();
+      }
+#pragma unroll
+      for (int u = 0; u < C::B_PT; ++u) {
+        int c = (tid + 256 * u) % CPR;
+        int k0 = kb + c * 8;
+        if (k0 < g.K)
+          rb[u].load(b_ptr[u] + k0);
+        else
+          rb[u].zero();
+      }
+    };
+    auto store_tile = [&](int stage) {
+      Chunk<T>* sa = smem + stage * C::STAGE;
+      Chunk<T>* sb = sa + BM * CPR;
+#pragma unroll
+      for (int u = 0; u < C::A_PT; ++u) {
+        int idx = tid + 256 * u;
+        if (idx >= BM * CPR) break;
+        int r = idx / CPR, c = idx % CPR;
+        ra[u].store(&sa[r * CPR + swz<CPR>(r, c)]);
+      }
+#pragma unroll
+      for (int u = 0; u < C::B_PT; ++u) {
+        int idx = tid + 256 * u;
+        if (idx >= BN * CPR) break;
+        int r = idx / CPR, c = idx % CPR;
+        rb[u].store(&sb[r * CPR + swz<CPR>(r, c)]);
+      }
+    };
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        load_frags(cur, ks, 0);
+        mma_step(0);
+      }
+      if (kt + 1 < nk) store_tile(cur ^ 1);
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue.  The fp32 tile goes through LDS in column slabs (phase 1:
-  // lane writes its column l32, rows 8*(r/4) + 4*g2 + r%4 of each 32x32 block);
-  // phase 2 walks the slab in 8-element chunks and writes 16-byte pieces.
+  // ---- epilogue.  The fp32 tile goes through LDS in column slabs; phase 2
+  // walks a slab in 8-element chunks and writes 16-byte pieces.
   float* slab = reinterpret_cast<float*>(smem_raw);
   constexpr int SW = C::SW, SWP = C::SWP;
 #pragma unroll
   for (int s0 = 0; s0 < BN; s0 += SW) {
-    // phase 1
+    // phase 1: the accumulators hold C^T (the weight fragment is the MFMA row
+    // operand), so element r of lane l is column 8*(r/4) + 4*g2 + r%4, row l32 of
+    // its 32x32 block: four consecutive columns per lane, one 16-byte LDS write
     if (brow0 + BN / WN > s0 && brow0 < s0 + SW) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = brow0 + 32 * j + l32 - s0;
-        if (col < 0 || col >= SW) continue;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int rq = 0; rq < 4; ++rq) {
+          const int col = brow0 + 32 * j + 8 * rq + 4 * g2 - s0;
+          if (col < 0 || col >= SW) continue;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = arow0 + 32 * i + 8 * (r / 4) + 4 * g2 + (r % 4);
-            slab[row * SWP + col] = acc[i][j][r];
+          for (int i = 0; i < TM; ++i) {
+            const int row = arow0 + 32 * i + l32;
+            const f32x4 q4 = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2], acc[i][j][4 * rq + 3]};
+            *reinterpret_cast<f32x4*>(&slab[row * SWP + col]) = q4;
           }
+        }
       }
     }
     __syncthreads();
@@ -365,6 +493,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   }
 }
 
+// The kernel body lives in a device function: the host pass only sees this wrapper.
+template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
+  gemm_body<T, BM, BN, WM, WN, LOADER, EPI>(g);
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   using C = Gemm<T, BM, BN, WM, WN, LOADER, EPI>;
@@ -400,6 +534,9 @@ hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
 template <typename T>
 hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
   if (g.M <= 0) return hipSuccess;
+  // the LDS-DMA path streams whole k-tiles: K must be a multiple of the k-tile depth
+  constexpr int BK = sizeof(T) == 2 ? 32 : 16;
+  if (loader == LOAD_PLAIN && g.K % BK != 0) return hipErrorInvalidValue;
   if (loader == LOAD_PATCH) {
     if (epi == EPI_STORE_F32) return launch_by_n<T, LOAD_PATCH, EPI_STORE_F32>(g, st);
     return hipErrorInvalidValue;
