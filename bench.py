@@ -181,7 +181,7 @@ def main():
         "block_tflops": round(block_tflops, 2),
         "step_tflop": round(flops / 1e12, 3),
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 3) for k, v in kt.items()},
-        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_kernel_1src<bf16,128>)",
+        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_kernel<bf16,128>)",
                      "achieved": round(attn_achieved, 2), "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / MI355X_BF16_TFLOPS, 4), "traffic": None,
                      "avg_launch_ms": round(attn_avg, 4), "launches": attn_n,

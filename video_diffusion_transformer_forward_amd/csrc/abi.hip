@@ -280,7 +280,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
   {
     AttnArgs a;
     a.q = at(ws, p.q); a.Lq = d.L; a.Lqp = d.Lp;
-    a.k[0] = at(ws, p.k); a.vt[0] = at(ws, p.vt); a.Lk[0] = d.L; a.Lkp[0] = d.Lp; a.nsrc = 1;
+    a.k[0] = at(ws, p.k); a.vt[0] = at(ws, p.vt); a.Lk[0] = d.L; a.Lkp[0] = d.Lp; a.nsrc = 1; a.self = 1;
     a.o = o; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
     HIP_TRY(timed(WAN_KERNEL_SELF_ATTENTION, st, [&] { return launch_attention<T>(a, st); }));
   }

@@ -10,7 +10,8 @@
 // probabilities go straight from the S^T accumulators into the B operand of
 // O^T = V^T P^T; v is stored transposed with 4-key runs permuted inside every
 // 16-key group so that each lane's eight keys are one 16-byte LDS read.
-// K and V^T tiles of 64 keys are double-buffered in LDS (XOR-swizzled rows),
+// K and V^T tiles of 64 keys are double-buffered in LDS (XOR-swizzled rows, so
+// the 16 rows one 16-lane group of a wide LDS read touches hit distinct banks),
 // the next tile's global loads overlapping the current tile's MFMAs.
 // The running max is only moved (and the accumulators rescaled) when it grows
 // by more than 2^8: the probabilities then stay below 256, and numerator and
@@ -27,6 +28,20 @@ constexpr float RESCALE_LOG2 = 8.0f;  // move the running max only when it grows
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Position of 16-byte chunk c in LDS row r.  A wave-wide 16-byte LDS read is
+// served 16 lanes at a time: the 16 rows those lanes touch must land on 16
+// distinct 16-byte bank groups (64 banks x 4 bytes = 256 bytes).
+// CPR is the number of chunks (8 elements each) per row.
+template <typename T, int CPR>
+__device__ __forceinline__ int att_swz(int r, int c) {
+  if constexpr (CPR >= 16)
+    return c ^ (r & 15);                   // 256-byte (or longer) rows all start on bank 0
+  else if constexpr (sizeof(T) == 2)
+    return c ^ ((r >> 1) & 7);             // 128-byte rows: two rows per bank line
+  else
+    return c ^ (r & 7);                    // float, 8 chunks of 32 bytes
+}
+
 template <typename T, int HD>
 struct AttCfg {
   static constexpr int HC = HD / 8;                       // chunks per K row
@@ -39,20 +54,23 @@ struct AttCfg {
   static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(Chunk<T>);
 };
 
-template <typename T, int HD, int NSRC>
+template <typename T, int HD, int NSRC, int KIND>
 __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   using Cfg = AttCfg<T, HD>;
   constexpr int HC = Cfg::HC;
   constexpr int SPC = Cfg::SPC;
-  constexpr int BMQ = 128;      // queries per workgroup: 4 waves x 32
-  constexpr int ND = HD / 32;   // 32-row blocks of d in O^T
-  constexpr int NS = HD / 16;   // 16-deep k steps of S^T
+  constexpr int CB = (int)sizeof(Chunk<T>);              // bytes per chunk
+  constexpr int BMQ = 128;                               // queries per workgroup: 4 waves x 32
+  constexpr int ND = HD / 32;                            // 32-row blocks of d in O^T
+  constexpr int NS = HD / 16;                            // 16-deep k steps of S^T
+  constexpr int STAGE_B = Cfg::STAGE * CB;               // bytes per LDS stage
+  constexpr int KBLK_B = 32 * HC * CB;                   // bytes of 32 K rows
+  constexpr int VBLK_B = 32 * 8 * CB;                    // bytes of 32 V^T rows
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  Chunk<T>* smem = reinterpret_cast<Chunk<T>*>(smem_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5;
   const int l32 = lane & 31;
 
@@ -80,30 +98,26 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     }
   }
 
-  // K / V^T tiles go global -> LDS directly; each wave instruction fills 1 KB of LDS,
-  // lane l the l-th 16 bytes, so the swizzle is applied on the global side.
-  auto issue_tile = [&](const T* Kp, const T* Vp, int Lkp, int j, int stage) {
-    unsigned char* kst = smem_raw + (size_t)stage * Cfg::STAGE * sizeof(Chunk<T>);
-    unsigned char* vst = kst + (size_t)Cfg::KCH * sizeof(Chunk<T>);
+  // Per-lane LDS byte offsets of the MFMA operands.  The swizzle of row
+  // 32*blk + l32 does not depend on blk, so the block and the stage enter as
+  // immediate offsets of the LDS reads.
+  int koff[NS], voff[4];
 #pragma unroll
-    for (int i = 0; i < Cfg::K_DMA; ++i) {
-      const int P = (wave * Cfg::K_DMA + i) * 64 + lane;   // 16-byte piece in the tile
-      const int pc = P / SPC, sub = P % SPC;               // physical chunk, piece within it
-      const int r = pc / HC, pcol = pc % HC;
-      const int lc = pcol ^ (r & 7);                       // logical chunk stored there
-      const T* src = Kp + (long long)(j * ATT_BN + r) * HD + lc * 8 + sub * (8 / SPC);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(kst + (size_t)(wave * Cfg::K_DMA + i) * 1024), 16, 0, 0);
-    }
+  for (int s = 0; s < NS; ++s) koff[s] = (l32 * HC + att_swz<T, HC>(l32, 2 * s + g2)) * CB;
 #pragma unroll
-    for (int i = 0; i < Cfg::V_DMA; ++i) {
-      const int P = (wave * Cfg::V_DMA + i) * 64 + lane;
-      const int pc = P / SPC, sub = P % SPC;
-      const int r = pc / 8, pcol = pc % 8;
-      const int lc = pcol ^ (r & 7);
-      const T* src = Vp + (long long)r * Lkp + j * ATT_BN + lc * 8 + sub * (8 / SPC);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(vst + (size_t)(wave * Cfg::V_DMA + i) * 1024), 16, 0, 0);
-    }
-  };
+  for (int u = 0; u < 4; ++u) voff[u] = Cfg::KCH * CB + (l32 * 8 + att_swz<T, 8>(l32, 2 * u + g2)) * CB;
+
+  // Per-lane element offsets of the global -> LDS copies inside one tile.  Each
+  // wave instruction fills 1 KB of LDS, lane l the l-th 16 bytes, so the XOR
+  // swizzle of the chunk position is applied to the global address.
+  int kdo[Cfg::K_DMA], vdo[Cfg::V_DMA];
+#pragma unroll
+  for (int i = 0; i < Cfg::K_DMA; ++i) {
+    const int P = (wave * Cfg::K_DMA + i) * 64 + lane;
+    const int pc = P / SPC, sub = P % SPC;
+    const int r = pc / HC;
+    kdo[i] = r * HD + att_swz<T, HC>(r, pc % HC) * 8 + sub * (8 / SPC);
+  }
 
   f32x16 o[ND];
   f32x16 o_prev[NSRC == 2 ? ND : 1];
@@ -114,6 +128,27 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const T* Kp = reinterpret_cast<const T*>(a.k[src]) + (long long)bh * Lkp * HD;
     const T* Vp = reinterpret_cast<const T*>(a.vt[src]) + (long long)bh * HD * Lkp;
     const int nkt = (Lk + ATT_BN - 1) / ATT_BN;
+#pragma unroll
+    for (int i = 0; i < Cfg::V_DMA; ++i) {
+      const int P = (wave * Cfg::V_DMA + i) * 64 + lane;
+      const int pc = P / SPC, sub = P % SPC;
+      const int r = pc / 8;
+      vdo[i] = r * Lkp + att_swz<T, 8>(r, pc % 8) * 8 + sub * (8 / SPC);
+    }
+
+    auto issue = [&](int j, int stage) {
+      unsigned char* kst = smem_raw + stage * STAGE_B;
+      const T* kt = Kp + (long long)j * ATT_BN * HD;
+#pragma unroll
+      for (int i = 0; i < Cfg::K_DMA; ++i)
+        __builtin_amdgcn_global_load_lds(kt + kdo[i], (lds_void*)(kst + (wave * Cfg::K_DMA + i) * 1024), 16, 0, 0);
+      unsigned char* vst = kst + Cfg::KCH * CB;
+      const T* vtile = Vp + j * ATT_BN;
+#pragma unroll
+      for (int i = 0; i < Cfg::V_DMA; ++i)
+        __builtin_amdgcn_global_load_lds(vtile + vdo[i], (lds_void*)(vst + (wave * Cfg::V_DMA + i) * 1024), 16, 0,
+                                         0);
+    };
 
     float m = -INFINITY, l = 0.f;
 #pragma unroll
@@ -121,25 +156,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-    issue_tile(Kp, Vp, Lkp, 0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int j = 0; j < nkt; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < nkt) issue_tile(Kp, Vp, Lkp, j + 1, cur ^ 1);
-      const Chunk<T>* ks = smem + cur * Cfg::STAGE;
-      const Chunk<T>* vs = ks + Cfg::KCH;
-
+    // one 64-key tile held in LDS stage `stage` (a literal after inlining)
+    auto tile = [&](int j, int stage) {
+      const unsigned char* sbase = smem_raw + stage * STAGE_B;
       // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks)
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + l32;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           Chunk<T> ka;
-          ka.load(&ks[row * HC + ((2 * s + g2) ^ (row & 7))]);
+          ka.load(sbase + kb * KBLK_B + koff[s]);
           if (s == 0) {
             f32x16 zero = {};
             sacc[kb] = zero;
@@ -147,9 +174,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
           mma32(sacc[kb], ka, qf[s]);
         }
       }
-
-      // online softmax in base 2; the scale enters through one FMA per score
-      float mx = -INFINITY;
+      // keys at or past Lk get -inf (only ever the last tile)
       if ((j + 1) * ATT_BN > Lk) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -159,12 +184,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
             if (key >= Lk) sacc[kb][r] = -INFINITY;
           }
       }
+      // online softmax in base 2; the scale enters through one FMA per score
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m, mx);
+        for (int r = 0; r < 16; r += 2)
+          mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[kb][r], sacc[kb][r + 1]));
+      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = __builtin_elementwise_maximum(m, mx);
       if (__ballot((mnew - m) * c > RESCALE_LOG2) != 0) {
         const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
         m = mnew;
@@ -188,21 +216,32 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
           }
           pack8(pf[2 * kb + half], p);
         }
-
       // O^T += V^T P^T, four 16-key steps
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const int row = 32 * db + l32;
           Chunk<T> va;
-          va.load(&vs[row * 8 + ((2 * u + g2) ^ (row & 7))]);
+          va.load(sbase + db * VBLK_B + voff[u]);
           mma32(o[db], va, pf[u]);
         }
       }
+    };
 
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int j = 0; j < nkt; j += 2) {
+      if (j + 1 < nkt) issue(j + 1, 1);
+      tile(j, 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (j + 1 < nkt) {
+        if (j + 2 < nkt) issue(j + 2, 0);
+        tile(j + 1, 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
     }
 
     // normalise this source
@@ -246,27 +285,35 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   }
 }
 
-// one key/value source: two workgroups per CU (at most 256 registers per lane)
+// Kernel entry points (thin wrappers: the host pass only sees these).  Self- and
+// text cross-attention run the same body under two symbols so that traces
+// separate them; KIND only keeps the instantiations apart.
+// One key/value source: two workgroups per CU (at most 256 registers per lane).
 template <typename T, int HD>
-__global__ __launch_bounds__(256, 2) void attn_kernel_1src(const AttnArgs a) {
-  attn_body<T, HD, 1>(a);
+__global__ __launch_bounds__(256, 2) void attn_self_kernel(const AttnArgs a) {
+  attn_body<T, HD, 1, 0>(a);
+}
+template <typename T, int HD>
+__global__ __launch_bounds__(256, 2) void attn_cross_kernel(const AttnArgs a) {
+  attn_body<T, HD, 1, 1>(a);
 }
 // image + text sources keep a second accumulator: one workgroup per CU
 template <typename T, int HD>
-__global__ __launch_bounds__(256, 1) void attn_kernel_2src(const AttnArgs a) {
-  attn_body<T, HD, 2>(a);
+__global__ __launch_bounds__(256, 1) void attn_cross2_kernel(const AttnArgs a) {
+  attn_body<T, HD, 2, 2>(a);
 }
 
 template <typename T, int HD, int NSRC>
 hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t st) {
   using Cfg = AttCfg<T, HD>;
-  auto kern = NSRC == 1 ? attn_kernel_1src<T, HD> : attn_kernel_2src<T, HD>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  auto kern = NSRC == 2 ? attn_cross2_kernel<T, HD> : (a.self ? attn_self_kernel<T, HD> : attn_cross_kernel<T, HD>);
+  static bool attr_set[2] = {false, false};
+  const int which = a.self ? 1 : 0;
+  if (!attr_set[which]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[which] = true;
   }
   const int nqt = (a.Lq + 127) / 128;
   const int G = nqt * a.heads * a.B;

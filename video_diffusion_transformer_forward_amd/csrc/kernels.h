@@ -57,6 +57,7 @@ struct AttnArgs {
   const void* vt[2] = {nullptr, nullptr};
   int Lk[2] = {0, 0}, Lkp[2] = {0, 0};
   int nsrc = 1;
+  int self = 0;  // 1: self-attention (selects the kernel symbol; the computation is the same)
   void* o = nullptr;
   int B = 1, heads = 1, hd = 128;
   float scale_log2 = 0.f;
