@@ -25,6 +25,19 @@ from video_diffusion_transformer_forward_amd import synth as S  # noqa: E402
 
 MI355X_BF16_TFLOPS = 2516.6   # dense bf16 MFMA peak (256 CU x 4096 flop/clk x 2.4 GHz)
 MI355X_FP32_TFLOPS = 157.3
+CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
+
+# L2 <-> memory bytes of one self-attention launch, from two counter-collection runs of
+# `bench.py --steps 1 --warmup 0 --no-cpu-baseline --calib-copy` (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch), each scaled by known/counted bytes of the 1 GiB calibration copy in the
+# same run.  Valid only for the kernel sources they were taken on (checked by hash).
+ATTN_COUNTERS = {
+    "fetch_kib": 1638730.42, "fetch_scale": 1048576 / 524306.46,
+    "write_kib": 196560.0, "write_scale": 1048576 / 1048576.0,
+    "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
+                "video_diffusion_transformer_forward_amd/csrc/common.h"),
+    "sha256": "9d97c2cb9732192fc8c1c2a785bddff549fcd19575854df9970445cac858a350",
+}
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 
 
@@ -56,6 +69,19 @@ def step_flops(cfg: S.WanConfig) -> float:
     return cfg.n_blocks * per_block + patch + head + time_mlp
 
 
+def attn_traffic_bytes():
+    """Counted bytes per self-attention launch, or None once its sources differ from the measured ones."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_COUNTERS["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != ATTN_COUNTERS["sha256"]:
+        return None
+    c = ATTN_COUNTERS
+    return round(c["fetch_kib"] * 1024 * c["fetch_scale"] + c["write_kib"] * 1024 * c["write_scale"])
+
+
 def cpu_baseline(cfg: S.WanConfig, budget_s: float = 20.0) -> dict:
     """The float64 oracle on a bounded sample of the same workload: one 1.3B block with the
     keys/values of all 32760 tokens and the outputs of a sample of query rows."""
@@ -66,7 +92,7 @@ def cpu_baseline(cfg: S.WanConfig, budget_s: float = 20.0) -> dict:
     mod = S.modulation(bcfg)
     ctx = S.context(bcfg, "cond")
     L, D, F = bcfg.seq_len, bcfg.dim, bcfg.ffn_dim
-    n_rows = 64
+    n_rows = 4096
     rows = np.linspace(0, L - 1, n_rows).astype(int).tolist()
     t0 = time.perf_counter()
     O.dit_block(x, mod, ctx, w, bcfg.heads, bcfg.grid, bcfg.img_len, rows=rows)
@@ -98,6 +124,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="wan13b_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB -> 1 GiB elementwise copy three times: the "
+                         "known-size kernel that scales the HBM byte counters of a counter-collection run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the hot path here is one GPU's share of the work "
@@ -147,6 +176,13 @@ def main():
                                            ("cross_attention", N.KERNEL_CROSS_ATTENTION),
                                            ("gemm", N.KERNEL_GEMM), ("elementwise", N.KERNEL_ELEMENTWISE))}
     assert bool(torch.isfinite(z).all())
+    if args.calib_copy:
+        src = torch.ones(CALIB_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_step = elapsed / args.steps * 1e3
     flops = step_flops(cfg)
@@ -183,7 +219,9 @@ def main():
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 3) for k, v in kt.items()},
         "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_kernel<bf16,128>)",
                      "achieved": round(attn_achieved, 2), "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_achieved / MI355X_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_achieved / MI355X_BF16_TFLOPS, 4), "traffic": attn_traffic_bytes(),
+                     "traffic_unit": "bytes per launch (L2-memory fetch + write counters)",
+                     "algorithmic_bytes": 4 * 2 * cfg.batch * cfg.heads * cfg.seq_len * cfg.head_dim * 2,
                      "avg_launch_ms": round(attn_avg, 4), "launches": attn_n,
                      "flop_per_launch": bf["self_attention"]},
     }

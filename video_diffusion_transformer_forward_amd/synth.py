@@ -118,9 +118,13 @@ def get_config(name: str) -> WanConfig:
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return rounded.astype(np.uint32).view(np.float32).reshape(a.shape)
+    u = a.view(np.uint32)
+    # 32-bit arithmetic: finite values never carry past bit 31 (only NaN payloads could)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(a.shape)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
