@@ -217,7 +217,7 @@ def main():
         "block_tflops": round(block_tflops, 2),
         "step_tflop": round(flops / 1e12, 3),
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 3) for k, v in kt.items()},
-        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_kernel<bf16,128>)",
+        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_wide_kernel<128,2,1,8>)",
                      "achieved": round(attn_achieved, 2), "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / MI355X_BF16_TFLOPS, 4), "traffic": attn_traffic_bytes(),
                      "traffic_unit": "bytes per launch (L2-memory fetch + write counters)",

@@ -285,6 +285,368 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Self-attention in bf16, software-pipelined.
+//
+// A workgroup of NW waves owns NW*32*QB queries of one (batch, head) and shares
+// every K / V^T tile among them (with NW = 8, two waves per SIMD and one
+// workgroup per CU); a wave holds QB 32-query blocks, so each K or V^T fragment
+// read from LDS feeds QB MFMAs.  The key-tile loop is software-pipelined inside
+// the wave: while the matrix core computes the scores S(t+1) of the next tile,
+// the VALU runs the softmax of tile t, and the P V products of tile t overlap
+// the rest of it and the row maxima of S(t+1).  Since the scores of tile t+1
+// and the values of tile t are read in the same iteration, K and V^T tiles live
+// in two separate LDS rings of NR stages each.
+constexpr int WIDE_NW = 8;  // waves per workgroup
+constexpr int WIDE_QB = 1;  // 32-query blocks per wave
+constexpr int WIDE_NR = 2;  // stages per K / V^T ring
+
+template <int HD, int NR, int QB, int NW>
+struct WideCfg {
+  static constexpr int WQ = 32 * QB;    // queries per wave
+  static constexpr int BMQ = NW * WQ;   // queries per workgroup
+  static constexpr int KT_B = ATT_BN * HD * 2;  // bytes per K tile
+  static constexpr int VT_B = HD * ATT_BN * 2;  // bytes per V^T tile
+  static constexpr int K_DMA = KT_B / (16 * 64 * NW);  // 16-byte loads per thread per tile
+  static constexpr int V_DMA = VT_B / (16 * 64 * NW);
+  static constexpr size_t RING_BYTES = (size_t)NR * (KT_B + VT_B);
+  static constexpr size_t EPI_BYTES = (size_t)BMQ * HD * 2;
+  static constexpr size_t LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+  static_assert(K_DMA * 16 * 64 * NW == KT_B && V_DMA * 16 * 64 * NW == VT_B, "DMA split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+// s_waitcnt vmcnt(N) only (gfx9 encoding; the other counters at their maximum)
+template <int N>
+__device__ __forceinline__ void att_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that waits for this wave's LDS reads but leaves its global
+// loads in flight.
+__device__ __forceinline__ void att_barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int HD, int NR, int QB, int NW>
+__device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
+  using T = bf16;
+  using Cfg = WideCfg<HD, NR, QB, NW>;
+  constexpr int WQ = Cfg::WQ, BMQ = Cfg::BMQ;
+  constexpr int HC = HD / 8;        // chunks per K row
+  constexpr int CB = 16;            // bytes per chunk
+  constexpr int ND = HD / 32;       // 32-row blocks of d in O^T
+  constexpr int NS = HD / 16;       // 16-deep k steps of S^T
+  constexpr int KBLK_B = 32 * HC * CB;
+  constexpr int VBLK_B = 32 * 8 * CB;
+  constexpr int VRING = NR * Cfg::KT_B;  // byte offset of the V^T ring
+  constexpr int INFLIGHT = (NR - 2) * (Cfg::K_DMA + Cfg::V_DMA);
+  static_assert(NR >= 2, "ring");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g2 = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int nqt = (a.Lq + BMQ - 1) / BMQ;
+  const int G = nqt * a.heads * a.B;
+  const int id = xcd_remap(blockIdx.x, G);
+  const int qt = id % nqt;
+  const int bh = id / nqt;
+  const int b = bh / a.heads;
+  const int h = bh - b * a.heads;
+  const int q0 = qt * BMQ + wave * WQ;
+  const float c = a.scale_log2;
+  const int Lk = a.Lk[0];
+  const int Lkp = a.Lkp[0];
+  const int n = (Lk + ATT_BN - 1) / ATT_BN;
+
+  // queries of this wave, two 32-query blocks: B operand chunks (query l32, d chunk 2s + g2)
+  Chunk<T> qf[QB][NS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = q0 + 32 * qb + l32;
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((long long)bh * a.Lqp + qrow) * HD;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (qrow < a.Lq)
+        qf[qb][s].load(qp + (2 * s + g2) * 8);
+      else
+        qf[qb][s].zero();
+    }
+  }
+
+  // per-lane LDS byte offsets of the MFMA operands within a K tile / V^T tile
+  int koff[NS], voff[4];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) koff[s] = (l32 * HC + att_swz<T, HC>(l32, 2 * s + g2)) * CB;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) voff[u] = (l32 * 8 + att_swz<T, 8>(l32, 2 * u + g2)) * CB;
+
+  // per-lane byte offsets of the global -> LDS copies inside one tile (lane l of
+  // a wave instruction fills the l-th 16 bytes of a 1 KB LDS block)
+  unsigned kdo[Cfg::K_DMA], vdo[Cfg::V_DMA];
+#pragma unroll
+  for (int i = 0; i < Cfg::K_DMA; ++i) {
+    const int P = (wave * Cfg::K_DMA + i) * 64 + lane;
+    const int r = P / HC;
+    kdo[i] = (unsigned)(r * HD + att_swz<T, HC>(r, P % HC) * 8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::V_DMA; ++i) {
+    const int P = (wave * Cfg::V_DMA + i) * 64 + lane;
+    const int r = P / 8;
+    vdo[i] = (unsigned)(r * Lkp + att_swz<T, 8>(r, P % 8) * 8) * 2u;
+  }
+  const unsigned char* Kg = reinterpret_cast<const unsigned char*>(a.k[0]) + (long long)bh * Lkp * HD * 2;
+  const unsigned char* Vg = reinterpret_cast<const unsigned char*>(a.vt[0]) + (long long)bh * HD * Lkp * 2;
+
+  auto issue_k = [&](int j, int stage) {
+    const unsigned char* src = Kg + (long long)j * Cfg::KT_B;
+    unsigned char* dst = smem_raw + stage * Cfg::KT_B;
+#pragma unroll
+    for (int i = 0; i < Cfg::K_DMA; ++i)
+      __builtin_amdgcn_global_load_lds(src + kdo[i], (lds_void*)(dst + (wave * Cfg::K_DMA + i) * 1024), 16, 0, 0);
+  };
+  auto issue_v = [&](int j, int stage) {
+    const unsigned char* src = Vg + (long long)j * ATT_BN * 2;
+    unsigned char* dst = smem_raw + VRING + stage * Cfg::VT_B;
+#pragma unroll
+    for (int i = 0; i < Cfg::V_DMA; ++i)
+      __builtin_amdgcn_global_load_lds(src + vdo[i], (lds_void*)(dst + (wave * Cfg::V_DMA + i) * 1024), 16, 0, 0);
+  };
+
+  // S^T of one 32-key block kb of the K tile in stage kst, for both query blocks
+  auto scores = [&](f32x16 (&s)[QB][2], int kst, int kb) {
+    const unsigned char* kbase = smem_raw + kst * Cfg::KT_B + kb * KBLK_B;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      Chunk<T> ka;
+      ka.load(kbase + koff[st]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (st == 0) {
+          const f32x16 zero = {};
+          s[qb][kb] = zero;
+        }
+        mma32(s[qb][kb], ka, qf[qb][st]);
+      }
+    }
+  };
+  // keys at or past Lk get -inf (only ever the last tile)
+  auto mask = [&](f32x16 (&s)[QB][2], int j) {
+    if ((j + 1) * ATT_BN > Lk) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j * ATT_BN + 32 * kb + 8 * (r / 4) + 4 * g2 + (r % 4);
+            if (key >= Lk) s[qb][kb][r] = -INFINITY;
+          }
+    }
+  };
+  // row maxima of both query blocks (the two lanes of a query exchange theirs)
+  auto rowmax = [&](const f32x16 (&s)[QB][2], float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          v = __builtin_elementwise_maximum(v, __builtin_elementwise_maximum(s[qb][kb][r], s[qb][kb][r + 1]));
+      mx[qb] = __builtin_elementwise_maximum(v, __shfl_xor(v, 32, 64));
+    }
+  };
+
+  f32x16 o[QB][ND];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+
+  // Lazy running max: a query's max moves only when its tile max exceeds it by
+  // more than 2^8; its sum is then scaled by alpha at once, the accumulators
+  // (only when some lane of the wave moved) once the pending P V products are in.
+  float alpha[QB];
+  auto new_max = [&](const float (&mx)[QB]) {
+    bool moved = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mnew = __builtin_elementwise_maximum(m[qb], mx[qb]);
+      const bool mv = (mnew - m[qb]) * c > RESCALE_LOG2;
+      const float al = __builtin_amdgcn_exp2f((m[qb] - mnew) * c);
+      alpha[qb] = mv ? al : 1.0f;
+      m[qb] = mv ? mnew : m[qb];
+      l[qb] *= alpha[qb];
+      moved = moved || mv;
+    }
+    return __ballot(moved) != 0;
+  };
+  auto scale_o = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
+  };
+  // probabilities of 32-key block kb for both query blocks -> B operand chunks pf[qb][2kb], pf[qb][2kb+1]
+  auto probs = [&](const f32x16 (&s)[QB][2], int kb, Chunk<T> (&pf)[QB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nmc = -m[qb] * c;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * half + e], c, nmc));
+          l[qb] += p[e];
+        }
+        pack8(pf[qb][2 * kb + half], p);
+      }
+    }
+  };
+  // O^T += V^T P^T over 16-key steps u0, u0+1 of the V^T tile in stage vst
+  auto pv = [&](int vst, int u0, const Chunk<T> (&pf)[QB][4]) {
+    const unsigned char* vbase = smem_raw + VRING + vst * Cfg::VT_B;
+#pragma unroll
+    for (int u = u0; u < u0 + 2; ++u)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        Chunk<T> va;
+        va.load(vbase + db * VBLK_B + voff[u]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mma32(o[qb][db], va, pf[qb][u]);
+      }
+  };
+
+  // Values computed in one phase and consumed in a later one are pinned where
+  // they are produced (an empty asm that takes them in registers); otherwise the
+  // compiler sinks their arithmetic next to the consuming MFMAs and the phases
+  // no longer overlap VALU work with matrix work.
+
+  // ---- prologue: K_0..K_{NR-1} and V_0..V_{NR-2} in flight; S(0), its maxima and
+  // the probabilities of its first 32 keys
+#pragma unroll
+  for (int j = 0; j < NR; ++j) issue_k(min(j, n - 1), j);
+#pragma unroll
+  for (int j = 0; j < NR - 1; ++j) issue_v(min(j, n - 1), j);
+  att_wait_vmcnt<0>();
+  __syncthreads();
+  f32x16 S[QB][2];
+  Chunk<T> pf[QB][4];
+  float mx[QB];
+  auto pin_probs = [&](int kb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(pf[qb][2 * kb].v), "+v"(pf[qb][2 * kb + 1].v));
+  };
+  auto pin_stats = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(m[qb]), "+v"(l[qb]), "+v"(alpha[qb]), "+v"(mx[qb]));
+  };
+  scores(S, 0, 0);
+  scores(S, 0, 1);
+  mask(S, 0);
+  rowmax(S, mx);
+  new_max(mx);  // first tile: the max moves from -inf, sums and accumulators are still zero
+  probs(S, 0, pf);
+  att_barrier_lds();  // K stage 0 is refilled by the first iteration
+
+  // One iteration, entered with the scores S(t) of tile t in S and the
+  // probabilities of its first 32 keys in pf[.][0..1]:
+  //   S(t+1) for keys 0..31 (MFMA)   | probabilities of tile t, keys 32..63 (VALU)
+  //   S(t+1) for keys 32..63 (MFMA)  |
+  //   O += P V, tile t keys 0..31    | masking and row maxima of S(t+1)
+  //   O += P V, tile t keys 32..63   | probabilities of tile t+1, keys 0..31
+  // K_{t+1} sits in K stage (t+1)%NR, V_t in V stage t%NR.  The loads issued here
+  // refill the stages read in the previous iteration: K_{t+NR} and V_{t+NR-1}
+  // (indices clamped at the last tile; those copies are never read).  Past the
+  // last tile S(n) is computed from a stale stage but masked out entirely.
+  // `ph` = t % NR, a literal after inlining, so every LDS offset is an immediate.
+  auto iter = [&](int t, int ph) {
+    const int kst = (ph + 1) % NR, vst = ph;
+    issue_k(min(t + NR, n - 1), ph);
+    issue_v(min(t + NR - 1, n - 1), (ph + NR - 1) % NR);
+    // the scheduler may interleave inside a phase, never across (that would take
+    // a second set of score registers)
+    scores(S, kst, 0);
+    probs(S, 1, pf);
+    pin_probs(1);
+    __builtin_amdgcn_sched_barrier(0);
+    scores(S, kst, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mask(S, t + 1);
+    pv(vst, 0, pf);
+    rowmax(S, mx);
+    const bool moved = new_max(mx);
+    pin_stats();
+    __builtin_amdgcn_sched_barrier(0);
+    pv(vst, 2, pf);
+    probs(S, 0, pf);
+    pin_probs(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (moved) scale_o();
+    att_wait_vmcnt<INFLIGHT>();  // K_{t+2} and V_{t+1} have landed
+    att_barrier_lds();
+  };
+  static_assert(NR == 2 || NR == 4, "ring depth");
+  for (int t = 0; t < n; t += NR) {
+    iter(t, 0);
+    if (t + 1 < n) iter(t + 1, 1);
+    if constexpr (NR == 4) {
+      if (t + 2 < n) iter(t + 2, 2);
+      if (t + 3 < n) iter(t + 3, 3);
+    }
+  }
+  att_wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- epilogue: normalise, stage the wave's 64 rows in LDS as [query][d], 16-byte row stores
+  T* stg = reinterpret_cast<T*>(smem_raw) + wave * (WQ * HD);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float inv = 1.0f / (l[qb] + __shfl_xor(l[qb], 32, 64));
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r / 4) + 4 * g2 + (r % 4);
+        stg[(32 * qb + l32) * HD + d] = from_f<T>(o[qb][db][r] * inv);
+      }
+  }
+  __syncthreads();
+  const int ld = a.heads * HD;
+#pragma unroll
+  for (int u = 0; u < (WQ * HC) / 64; ++u) {
+    const int idx = lane + 64 * u;
+    const int qr = idx / HC, cc = idx % HC;
+    const int q = q0 + qr;
+    if (q < a.Lq) {
+      Chunk<T> v;
+      v.load(stg + qr * HD + cc * 8);
+      v.store(reinterpret_cast<T*>(a.o) + ((long long)b * a.Lq + q) * ld + h * HD + cc * 8);
+    }
+  }
+}
+
 // Kernel entry points (thin wrappers: the host pass only sees these).  Self- and
 // text cross-attention run the same body under two symbols so that traces
 // separate them; KIND only keeps the instantiations apart.
@@ -296,6 +658,11 @@ __global__ __launch_bounds__(256, 2) void attn_self_kernel(const AttnArgs a) {
 template <typename T, int HD>
 __global__ __launch_bounds__(256, 2) void attn_cross_kernel(const AttnArgs a) {
   attn_body<T, HD, 1, 1>(a);
+}
+// bf16 self-attention: 8 waves of 32 queries (or 4 waves of 32*QB) per workgroup
+template <int HD, int NR, int QB, int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && QB == 1) ? 2 : 1) void attn_self_wide_kernel(const AttnArgs a) {
+  attn_wide_body<HD, NR, QB, NW>(a);
 }
 // image + text sources keep a second accumulator: one workgroup per CU
 template <typename T, int HD>
@@ -323,9 +690,29 @@ hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
+template <int HD, int NR, int QB, int NW>
+hipError_t launch_attn_wide(const AttnArgs& a, hipStream_t st) {
+  using Cfg = WideCfg<HD, NR, QB, NW>;
+  auto kern = attn_self_wide_kernel<HD, NR, QB, NW>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nqt = (a.Lq + Cfg::BMQ - 1) / Cfg::BMQ;
+  const int G = nqt * a.heads * a.B;
+  hipLaunchKernelGGL(kern, dim3(G), dim3(64 * NW), Cfg::LDS_BYTES, st, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.Lq <= 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2) {
+    if (a.hd == 128 && a.nsrc == 1 && a.self) return launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW>(a, st);
+  }
   if (a.hd == 128) {
     if (a.nsrc == 1) return launch_attn_cfg<T, 128, 1>(a, st);
     return launch_attn_cfg<T, 128, 2>(a, st);

@@ -20,11 +20,11 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int NST_, int LOADER, int EPI>
 struct Gemm {
   static constexpr int BK = sizeof(T) == 2 ? 32 : 16;  // 64-byte tile rows
   static constexpr int CPR = BK / 8;                   // chunks per tile row (4 bf16, 2 float)
-  static constexpr int NST = 4;                        // LDS ring stages
+  static constexpr int NST = NST_;                     // LDS ring stages
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
   static constexpr int STAGE = (BM + BN) * CPR;  // chunks per stage
@@ -45,6 +45,7 @@ struct Gemm {
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA split");
   static_assert(CPR * sizeof(Chunk<T>) == 64, "64-byte rows");
+  static_assert(NST >= 3 && NST <= 4, "ring depth");
 };
 
 // physical chunk position of logical chunk c in tile row r
@@ -103,9 +104,9 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int NST_, int LOADER, int EPI>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-  using C = Gemm<T, BM, BN, WM, WN, LOADER, EPI>;
+  using C = Gemm<T, BM, BN, WM, WN, NST_, LOADER, EPI>;
   constexpr int BK = C::BK, CPR = C::CPR, TM = C::TM, TN = C::TN, NST = C::NST;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Chunk<T>* smem = reinterpret_cast<Chunk<T>*>(smem_raw);
@@ -213,10 +214,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         __builtin_amdgcn_global_load_lds(b_src[i] + koff, (lds_void*)(bbase + (size_t)(wave * NB + i) * 1024), 16,
                                          0, 0);
     };
-    static_assert(NST == 4 && (KS == 1 || KS == 2), "ring of 4, one or two k steps per tile");
+    static_assert(KS == 1 || KS == 2, "one or two k steps per tile");
     // Every iteration issues one k-tile (the index clamped at the end, the
-    // redundant copies landing in stages nobody reads again), so exactly two
+    // redundant copies landing in stages nobody reads again), so exactly NST-2
     // tiles may stay in flight when the next one is needed.
+    constexpr int INFLIGHT = (NST - 2) * DPT;
     auto issue_c = [&](int kt) { issue(min(kt, nk - 1)); };
     // the LDS reads of the next fragments interleaved with the MFMAs of this step
     auto interleave = [&]() {
@@ -229,7 +231,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
 #pragma unroll
     for (int s0 = 0; s0 < NST - 1; ++s0) issue_c(s0);
-    wait_vmcnt<2 * DPT>();
+    wait_vmcnt<INFLIGHT>();
     barrier_lds();
     load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -240,7 +242,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         interleave();
         // refill the stage of k-tile kt-1 (its last reads preceded the previous barrier)
         issue_c(kt + NST - 1);
-        wait_vmcnt<2 * DPT>();  // k-tile kt+1 has landed
+        wait_vmcnt<INFLIGHT>();  // k-tile kt+1 has landed
         barrier_lds();
         load_frags((kt + 1) % NST, 0, 0);
         mma_step(1);
@@ -248,7 +250,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       } else {
         issue_c(kt + NST - 1);
         mma_step(0);
-        wait_vmcnt<2 * DPT>();
+        wait_vmcnt<INFLIGHT>();
         barrier_lds();
         load_frags((kt + 1) % NST, 0, 0);
       }
@@ -494,16 +496,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 }
 
 // The kernel body lives in a device function: the host pass only sees this wrapper.
-template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
-  gemm_body<T, BM, BN, WM, WN, LOADER, EPI>(g);
+// OCC workgroups share a CU (it bounds the registers per wave).
+template <typename T, int BM, int BN, int WM, int WN, int NST, int OCC, int LOADER, int EPI>
+__global__ __launch_bounds__(256, OCC) void gemm_kernel(const GemmArgs g) {
+  gemm_body<T, BM, BN, WM, WN, NST, LOADER, EPI>(g);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int LOADER, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int NST, int OCC, int LOADER, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
-  using C = Gemm<T, BM, BN, WM, WN, LOADER, EPI>;
+  using C = Gemm<T, BM, BN, WM, WN, NST, LOADER, EPI>;
+  static_assert(OCC * C::LDS_BYTES <= 160 * 1024, "occupancy exceeds the LDS");
   if (g.N % BN != 0) return hipErrorInvalidValue;
-  auto kern = gemm_kernel<T, BM, BN, WM, WN, LOADER, EPI>;
+  auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, OCC, LOADER, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -520,11 +524,17 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 template <typename T, int LOADER, int EPI>
 hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 2, 2, LOADER, EPI>(g, st);
-    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, LOADER, EPI>(g, st);
+    // Short-K GEMMs with a heavy epilogue (GELU, residual read-modify-write):
+    // 256x128 tiles and a three-stage ring (72 KB) give two workgroups per CU,
+    // so one workgroup's epilogue overlaps the other's main loop.  Otherwise
+    // 256x256 tiles (one workgroup per CU) read the fewest operand bytes.
+    constexpr bool heavy_epi = EPI == EPI_STORE_GELU || EPI == EPI_RESID;
+    if (heavy_epi && g.K <= 2048 && g.N % 128 == 0) return launch_cfg<T, 256, 128, 2, 2, 3, 2, LOADER, EPI>(g, st);
+    if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 2, 2, 4, 1, LOADER, EPI>(g, st);
+    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 1, LOADER, EPI>(g, st);
   } else {
-    if (g.N % 128 == 0) return launch_cfg<T, 128, 128, 2, 2, LOADER, EPI>(g, st);
-    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, LOADER, EPI>(g, st);
+    if (g.N % 128 == 0) return launch_cfg<T, 128, 128, 2, 2, 4, 1, LOADER, EPI>(g, st);
+    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 1, LOADER, EPI>(g, st);
   }
   return hipErrorInvalidValue;
 }
