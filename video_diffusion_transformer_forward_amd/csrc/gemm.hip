@@ -1,6 +1,6 @@
 // LDS-tiled MFMA GEMM for gfx950: C = A W^T + bias with fused epilogues.
 //
-// 256 threads (4 waves) per workgroup compute a BM x BN tile in BK-deep
+// WM x WN waves per workgroup (4 or 8) compute a BM x BN tile in BK-deep
 // k-tiles.  Operand tiles stream global -> LDS through the 16-byte LDS-DMA
 // path into an NST-stage ring, so the loads of a k-tile are issued NST-1 tiles
 // ahead of its MFMAs; one barrier per k-tile.  Inside a k-tile the MFMA operand
@@ -20,20 +20,24 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <typename T, int BM, int BN, int WM, int WN, int NST_, int LOADER, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int NST_, int RB, int LOADER, int EPI>
 struct Gemm {
-  static constexpr int BK = sizeof(T) == 2 ? 32 : 16;  // 64-byte tile rows
-  static constexpr int CPR = BK / 8;                   // chunks per tile row (4 bf16, 2 float)
+  static constexpr int BK = RB / (int)sizeof(T);       // k-tile depth
+  static constexpr int CPR = BK / 8;                   // chunks per tile row
+  static constexpr int PPR = RB / 16;                  // 16-byte pieces per tile row
+  static constexpr int RPD = 64 / PPR;                 // tile rows per LDS-DMA wave instruction
   static constexpr int NST = NST_;                     // LDS ring stages
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
   static constexpr int STAGE = (BM + BN) * CPR;  // chunks per stage
   static constexpr size_t PIPE_BYTES = (size_t)NST * STAGE * sizeof(Chunk<T>);
-  // DMA instructions per wave per k-tile: each covers 16 rows of 64 bytes
-  static constexpr int NA = BM / 64, NB = BN / 64;
+  // DMA instructions per wave per k-tile: each covers RPD rows
+  static constexpr int NW = WM * WN;                   // waves per workgroup
+  static constexpr int NT = 64 * NW;                   // threads per workgroup
+  static constexpr int NA = BM / RPD / NW, NB = BN / RPD / NW;
   // register-staged (gathered) path: chunks per thread per k-tile
-  static constexpr int A_PT = (BM * CPR + 255) / 256;
-  static constexpr int B_PT = (BN * CPR + 255) / 256;
+  static constexpr int A_PT = (BM * CPR + NT - 1) / NT;
+  static constexpr int B_PT = (BN * CPR + NT - 1) / NT;
   // epilogue slab: the whole tile when it fits the pipeline's LDS, else one wave column
   static constexpr int SW = ((size_t)BM * (BN + 4) * 4 <= PIPE_BYTES) ? BN : BN / WN;
   static constexpr int SWP = SW + 4;
@@ -41,17 +45,25 @@ struct Gemm {
   static constexpr size_t LDS_BYTES = PIPE_BYTES > SLAB_BYTES ? PIPE_BYTES : SLAB_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(BN % SW == 0 && SW % 8 == 0, "slab");
-  static_assert(WM * WN == 4, "4 waves");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA split");
-  static_assert(CPR * sizeof(Chunk<T>) == 64, "64-byte rows");
-  static_assert(NST >= 3 && NST <= 4, "ring depth");
+  static_assert(NA * RPD * NW == BM && NB * RPD * NW == BN, "DMA split");
+  static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
 };
 
-// physical chunk position of logical chunk c in tile row r
-template <int CPR>
+// Physical chunk position of logical chunk c in tile row r (RB-byte rows).  A
+// wave-wide 16-byte LDS read is served 16 lanes at a time; those lanes read 16
+// consecutive rows at one chunk, which must land on 16 distinct 16-byte bank
+// groups of the 256-byte bank line: 64-byte rows put 4 rows on a line and XOR
+// the chunk with row bits 2..3, 128-byte rows put 2 rows on a line and XOR the
+// 16-byte piece with row bits 1..3.
+template <int RB, int CPR>
 __device__ __forceinline__ int swz(int r, int c) {
-  return c ^ ((r >> 2) & (CPR - 1));
+  if constexpr (RB == 64)
+    return c ^ ((r >> 2) & (CPR - 1));
+  else
+    return c ^ ((r >> 1) & (CPR - 1));
 }
 
 // Load the 8 patch features [k0, k0+8) of token row (b, t): two channels x (2x2).
@@ -104,10 +116,10 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int NST_, int LOADER, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int NST_, int RB, int LOADER, int EPI>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-  using C = Gemm<T, BM, BN, WM, WN, NST_, LOADER, EPI>;
-  constexpr int BK = C::BK, CPR = C::CPR, TM = C::TM, TN = C::TN, NST = C::NST;
+  using C = Gemm<T, BM, BN, WM, WN, NST_, RB, LOADER, EPI>;
+  constexpr int BK = C::BK, CPR = C::CPR, TM = C::TM, TN = C::TN, NST = C::NST, NT = C::NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Chunk<T>* smem = reinterpret_cast<Chunk<T>*>(smem_raw);
 
@@ -163,12 +175,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = arow0 + 32 * i + l32;
-      fa[buf][i].load(&sa[r * CPR + swz<CPR>(r, c)]);
+      fa[buf][i].load(&sa[r * CPR + swz<RB, CPR>(r, c)]);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = brow0 + 32 * j + l32;
-      fb[buf][j].load(&sb[r * CPR + swz<CPR>(r, c)]);
+      fb[buf][j].load(&sb[r * CPR + swz<RB, CPR>(r, c)]);
     }
   };
   auto mma_step = [&](int buf) {
@@ -179,27 +191,27 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   };
 
   if constexpr (LOADER == LOAD_PLAIN) {
-    // ---- LDS-DMA ring.  One wave instruction fills 1 KB = 16 rows of 64 bytes;
-    // lane l writes the l-th 16 bytes, so the chunk swizzle is applied to the
-    // global address each lane reads.
+    // ---- LDS-DMA ring.  One wave instruction fills 1 KB = RPD tile rows; lane
+    // l writes the l-th 16 bytes, so the chunk swizzle is applied to the global
+    // address each lane reads.
     constexpr int SPC = (int)sizeof(Chunk<T>) / 16;
-    constexpr int NA = C::NA, NB = C::NB, DPT = NA + NB;
-    const int pp = lane & 3;          // 16-byte piece within the 64-byte row
-    const int rlow = lane >> 2;       // row within the instruction's 16 rows
-    const int col_off = swz<CPR>(rlow, pp / SPC) * 8 + (pp % SPC) * (8 / SPC);
+    constexpr int NA = C::NA, NB = C::NB, DPT = NA + NB, RPD = C::RPD, PPR = C::PPR;
+    const int pp = lane % PPR;   // 16-byte piece within the tile row
+    const int rlow = lane / PPR; // row within the instruction's RPD rows
+    auto col_off = [&](int r) { return swz<RB, CPR>(r, pp / SPC) * 8 + (pp % SPC) * (8 / SPC); };
     const T* a_src[NA];
     const T* b_src[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      int r = m0 + (wave * NA + i) * 16 + rlow;
-      r = min(r, g.M - 1);
+      const int rt = (wave * NA + i) * RPD + rlow;  // row within the tile
+      const int r = min(m0 + rt, g.M - 1);
       const int bb = r / g.a_rpb, t = r - bb * g.a_rpb;
-      a_src[i] = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda + col_off;
+      a_src[i] = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda + col_off(rt);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int r = n0 + (wave * NB + i) * 16 + rlow;
-      b_src[i] = reinterpret_cast<const T*>(g.Wt) + (long long)r * g.ldw + col_off;
+      const int rt = (wave * NB + i) * RPD + rlow;
+      b_src[i] = reinterpret_cast<const T*>(g.Wt) + (long long)(n0 + rt) * g.ldw + col_off(rt);
     }
     auto issue = [&](int kt) {
       unsigned char* base = smem_raw + (size_t)(kt % NST) * C::STAGE * sizeof(Chunk<T>);
@@ -214,10 +226,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         __builtin_amdgcn_global_load_lds(b_src[i] + koff, (lds_void*)(bbase + (size_t)(wave * NB + i) * 1024), 16,
                                          0, 0);
     };
-    static_assert(KS == 1 || KS == 2, "one or two k steps per tile");
-    // Every iteration issues one k-tile (the index clamped at the end, the
-    // redundant copies landing in stages nobody reads again), so exactly NST-2
-    // tiles may stay in flight when the next one is needed.
+    static_assert(KS == 1 || KS % 2 == 0, "one or an even number of k steps per tile");
+    // Every iteration first refills the stage of k-tile kt-1 (its last reads
+    // preceded the previous barrier) with k-tile kt+NST-1 (the index clamped at
+    // the end, the redundant copies landing in stages nobody reads again), so
+    // exactly NST-2 tiles may stay in flight when tile kt+1 is needed.
     constexpr int INFLIGHT = (NST - 2) * DPT;
     auto issue_c = [&](int kt) { issue(min(kt, nk - 1)); };
     // the LDS reads of the next fragments interleaved with the MFMAs of this step
@@ -231,24 +244,26 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
 #pragma unroll
     for (int s0 = 0; s0 < NST - 1; ++s0) issue_c(s0);
-    wait_vmcnt<INFLIGHT>();
+    wait_vmcnt<NST == 2 ? 0 : INFLIGHT>();
     barrier_lds();
     load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt % NST;
-      if constexpr (KS == 2) {
-        load_frags(cur, 1, 1);
-        mma_step(0);
-        interleave();
-        // refill the stage of k-tile kt-1 (its last reads preceded the previous barrier)
-        issue_c(kt + NST - 1);
+      issue_c(kt + NST - 1);
+      if constexpr (KS >= 2) {
+        // k steps 0 .. KS-2 with the fragments of the next step loading meanwhile
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+          load_frags(cur, ks + 1, (ks + 1) & 1);
+          mma_step(ks & 1);
+          interleave();
+        }
         wait_vmcnt<INFLIGHT>();  // k-tile kt+1 has landed
         barrier_lds();
         load_frags((kt + 1) % NST, 0, 0);
-        mma_step(1);
+        mma_step((KS - 1) & 1);
         interleave();
       } else {
-        issue_c(kt + NST - 1);
         mma_step(0);
         wait_vmcnt<INFLIGHT>();
         barrier_lds();
@@ -263,7 +278,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     int pf[C::A_PT], pi[C::A_PT], pj[C::A_PT], pzb[C::A_PT];
 #pragma unroll
     for (int u = 0; u < C::A_PT; ++u) {
-      int idx = min(tid + 256 * u, BM * CPR - 1);
+      int idx = min(tid + NT * u, BM * CPR - 1);
       int r = m0 + idx / CPR;
       r = min(r, g.M - 1);
       int b = r / g.c_rpb, t = r - b * g.c_rpb;
@@ -277,7 +292,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const T* b_ptr[C::B_PT];
 #pragma unroll
     for (int u = 0; u < C::B_PT; ++u) {
-      int idx = min(tid + 256 * u, BN * CPR - 1);
+      int idx = min(tid + NT * u, BN * CPR - 1);
       b_ptr[u] = reinterpret_cast<const T*>(g.Wt) + (long long)(n0 + idx / CPR) * g.ldw;
     }
     Chunk<T> ra[C::A_PT], rb[C::B_PT];
@@ -285,7 +300,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       const int kb = kt * BK;
 #pragma unroll
       for (int u = 0; u < C::A_PT; ++u) {
-        int c = (tid + 256 * u) % CPR;
+        int c = (tid + NT * u) % CPR;
         int k0 = kb + c * 8;
         if (k0 < g.K)
           load_patch_chunk<T>(ra[u], g, pzb[u], pf[u], pi[u], pj[u], k0);
@@ -294,7 +309,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
 #pragma unroll
       for (int u = 0; u < C::B_PT; ++u) {
-        int c = (tid + 256 * u) % CPR;
+        int c = (tid + NT * u) % CPR;
         int k0 = kb + c * 8;
         if (k0 < g.K)
           rb[u].load(b_ptr[u] + k0);
@@ -307,17 +322,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       Chunk<T>* sb = sa + BM * CPR;
 #pragma unroll
       for (int u = 0; u < C::A_PT; ++u) {
-        int idx = tid + 256 * u;
+        int idx = tid + NT * u;
         if (idx >= BM * CPR) break;
         int r = idx / CPR, c = idx % CPR;
-        ra[u].store(&sa[r * CPR + swz<CPR>(r, c)]);
+        ra[u].store(&sa[r * CPR + swz<RB, CPR>(r, c)]);
       }
 #pragma unroll
       for (int u = 0; u < C::B_PT; ++u) {
-        int idx = tid + 256 * u;
+        int idx = tid + NT * u;
         if (idx >= BN * CPR) break;
         int r = idx / CPR, c = idx % CPR;
-        rb[u].store(&sb[r * CPR + swz<CPR>(r, c)]);
+        rb[u].store(&sb[r * CPR + swz<RB, CPR>(r, c)]);
       }
     };
     load_tile(0);
@@ -369,7 +384,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     if (EPI == EPI_PACK && sec == 2) {
       // v^T: a chunk is 8 consecutive tokens of one feature column
       const int nv0 = nbase - g.nq - g.nk;
-      for (int idx = tid; idx < SW * (BM / 8); idx += 256) {
+      for (int idx = tid; idx < SW * (BM / 8); idx += NT) {
         const int col = idx % SW;
         const int r8 = (idx / SW) * 8;
         const int nvc = nv0 + col;
@@ -398,7 +413,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         }
       }
     } else {
-      for (int idx = tid; idx < BM * (SW / 8); idx += 256) {
+      for (int idx = tid; idx < BM * (SW / 8); idx += NT) {
         const int lrow = idx / (SW / 8);
         const int c8 = (idx % (SW / 8)) * 8;
         const int row = m0 + lrow;
@@ -497,17 +512,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
 // The kernel body lives in a device function: the host pass only sees this wrapper.
 // OCC workgroups share a CU (it bounds the registers per wave).
-template <typename T, int BM, int BN, int WM, int WN, int NST, int OCC, int LOADER, int EPI>
-__global__ __launch_bounds__(256, OCC) void gemm_kernel(const GemmArgs g) {
-  gemm_body<T, BM, BN, WM, WN, NST, LOADER, EPI>(g);
+template <typename T, int BM, int BN, int WM, int WN, int NST, int RB, int OCC, int LOADER, int EPI>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_kernel(const GemmArgs g) {
+  gemm_body<T, BM, BN, WM, WN, NST, RB, LOADER, EPI>(g);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int NST, int OCC, int LOADER, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int NST, int RB, int OCC, int LOADER, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
-  using C = Gemm<T, BM, BN, WM, WN, NST, LOADER, EPI>;
+  using C = Gemm<T, BM, BN, WM, WN, NST, RB, LOADER, EPI>;
   static_assert(OCC * C::LDS_BYTES <= 160 * 1024, "occupancy exceeds the LDS");
   if (g.N % BN != 0) return hipErrorInvalidValue;
-  auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, OCC, LOADER, EPI>;
+  if (LOADER == LOAD_PLAIN && g.K % C::BK != 0) return hipErrorInvalidValue;
+  auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, RB, OCC, LOADER, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -517,7 +533,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   }
   const int nm = (g.M + BM - 1) / BM;
   const int nt = nm * (g.N / BN);
-  hipLaunchKernelGGL(kern, dim3(nt), dim3(256), C::LDS_BYTES, st, g);
+  hipLaunchKernelGGL(kern, dim3(nt), dim3(C::NT), C::LDS_BYTES, st, g);
   return hipGetLastError();
 }
 
@@ -525,16 +541,18 @@ template <typename T, int LOADER, int EPI>
 hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     // Short-K GEMMs with a heavy epilogue (GELU, residual read-modify-write):
-    // 256x128 tiles and a three-stage ring (72 KB) give two workgroups per CU,
-    // so one workgroup's epilogue overlaps the other's main loop.  Otherwise
-    // 256x256 tiles (one workgroup per CU) read the fewest operand bytes.
+    // 256x128 tiles of 4 waves and a three-stage ring (72 KB) give two
+    // workgroups per CU, so one workgroup's epilogue overlaps the other's main
+    // loop.  Otherwise 256x256 tiles of 8 waves (two per SIMD, 64x128 each) and
+    // a four-stage ring: one workgroup per CU, the fewest operand bytes per flop,
+    // and a second wave on every SIMD to cover barrier and LDS waits.
     constexpr bool heavy_epi = EPI == EPI_STORE_GELU || EPI == EPI_RESID;
-    if (heavy_epi && g.K <= 2048 && g.N % 128 == 0) return launch_cfg<T, 256, 128, 2, 2, 3, 2, LOADER, EPI>(g, st);
-    if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 2, 2, 4, 1, LOADER, EPI>(g, st);
-    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 1, LOADER, EPI>(g, st);
+    if (heavy_epi && g.K <= 2048 && g.N % 128 == 0) return launch_cfg<T, 256, 128, 2, 2, 3, 64, 2, LOADER, EPI>(g, st);
+    if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOADER, EPI>(g, st);
+    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOADER, EPI>(g, st);
   } else {
-    if (g.N % 128 == 0) return launch_cfg<T, 128, 128, 2, 2, 4, 1, LOADER, EPI>(g, st);
-    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 1, LOADER, EPI>(g, st);
+    if (g.N % 128 == 0) return launch_cfg<T, 128, 128, 2, 2, 4, 64, 1, LOADER, EPI>(g, st);
+    if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOADER, EPI>(g, st);
   }
   return hipErrorInvalidValue;
 }
