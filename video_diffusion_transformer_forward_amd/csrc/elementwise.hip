@@ -12,6 +12,79 @@ constexpr int LN_MAX_V4 = 20;  // up to D = 5120 per wave (20 float4 per lane)
 
 // One wave per row: the row stays in registers between the mean, the variance
 // and the output pass (two-pass statistics, biased variance, eps 1e-6).
+// Narrow rows (D = 256*NV up to 2048): one wave walks R consecutive rows, the
+// next row's loads in flight while the current one is reduced, and keeps the
+// modulation vectors of its batch item in registers instead of re-reading them
+// for every row.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void ln_mod_rows_kernel(const float* __restrict__ x, T* __restrict__ out, int rows,
+                                                          int R, int rows_per_batch, const float* __restrict__ shift,
+                                                          const float* __restrict__ scale, long long mod_bstride) {
+  constexpr int D = NV * 256;
+  const int lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (r0 >= rows) return;
+  const int r1 = min(r0 + R, rows);
+  float4 v[NV], nx[NV], sc4[NV], sh4[NV];
+  int bcur = -1;
+  auto load_row = [&](float4 (&dst)[NV], int row) {
+    const float4* xr = reinterpret_cast<const float4*>(x + (long long)row * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) dst[i] = xr[i * 64 + lane];
+  };
+  load_row(v, r0);
+  for (int row = r0; row < r1; ++row) {
+    if (row + 1 < r1) load_row(nx, row + 1);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const float mean = wave_sum(s) * (1.0f / D);
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + 1e-6f);
+    if (scale) {
+      const int b = row / rows_per_batch;
+      if (b != bcur) {
+        bcur = b;
+        const float4* sc = reinterpret_cast<const float4*>(scale + (long long)b * mod_bstride);
+        const float4* sh = reinterpret_cast<const float4*>(shift + (long long)b * mod_bstride);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          sc4[i] = sc[i * 64 + lane];
+          sh4[i] = sh[i * 64 + lane];
+        }
+      }
+    }
+    T* orow = out + (long long)row * D;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int col = (i * 64 + lane) * 4;
+      float r[4] = {(v[i].x - mean) * rstd, (v[i].y - mean) * rstd, (v[i].z - mean) * rstd, (v[i].w - mean) * rstd};
+      if (scale) {
+        r[0] = r[0] * (1.f + sc4[i].x) + sh4[i].x;
+        r[1] = r[1] * (1.f + sc4[i].y) + sh4[i].y;
+        r[2] = r[2] * (1.f + sc4[i].z) + sh4[i].z;
+        r[3] = r[3] * (1.f + sc4[i].w) + sh4[i].w;
+      }
+      if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = to_bf16(r[e]);
+        *reinterpret_cast<bf16x4*>(orow + col) = o4;
+      } else {
+        *reinterpret_cast<float4*>(orow + col) = make_float4(r[0], r[1], r[2], r[3]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = nx[i];
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, T* __restrict__ out, int rows,
                                                      int D, int rows_per_batch, const float* __restrict__ shift,
@@ -185,8 +258,18 @@ hipError_t launch_ln_mod(const float* x, void* out, int rows, int D, int rows_pe
                          const float* scale, long long mod_bstride, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (D % 256 != 0 || D / 256 > LN_MAX_V4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(ln_mod_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, x, reinterpret_cast<T*>(out), rows,
-                     D, rows_per_batch, shift, scale, mod_bstride);
+  if ((shift == nullptr) != (scale == nullptr)) return hipErrorInvalidValue;
+  constexpr int R = 8;  // rows per wave in the narrow-row kernel
+  const dim3 grid_r((rows + 4 * R - 1) / (4 * R));
+  T* o = reinterpret_cast<T*>(out);
+  switch (D / 256) {
+    case 1: hipLaunchKernelGGL((ln_mod_rows_kernel<T, 1>), grid_r, dim3(256), 0, st, x, o, rows, R, rows_per_batch, shift, scale, mod_bstride); break;
+    case 2: hipLaunchKernelGGL((ln_mod_rows_kernel<T, 2>), grid_r, dim3(256), 0, st, x, o, rows, R, rows_per_batch, shift, scale, mod_bstride); break;
+    case 6: hipLaunchKernelGGL((ln_mod_rows_kernel<T, 6>), grid_r, dim3(256), 0, st, x, o, rows, R, rows_per_batch, shift, scale, mod_bstride); break;
+    default:
+      hipLaunchKernelGGL(ln_mod_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, x, o, rows, D, rows_per_batch,
+                         shift, scale, mod_bstride);
+  }
   return hipGetLastError();
 }
 
