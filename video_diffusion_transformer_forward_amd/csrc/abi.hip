@@ -22,6 +22,8 @@ constexpr int TIME_DIM = 256;
 
 size_t al(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 int pad64(int x) { return (x + 63) / 64 * 64; }
+// row pitch of the packing GEMMs: every 256-row tile lies inside one batch item
+int pad256(int x) { return (x + 255) / 256 * 256; }
 
 struct Dims {
   int B, Cin, F, H, W, Hh, Ww, L, Lp, D, heads, hd, Ff, Lt, Li, Lc, Ltp, Lip, mode;
@@ -69,7 +71,7 @@ int check_shape(const wan_shape* s, Dims* d) {
 
 // Offsets (bytes) inside the workspace of one block run over Bb batch rows.
 struct BlockPlan {
-  size_t m, r1, q, k, vt, o, ck, cvt, ik, ivt, rope, total;
+  size_t m, r1, q, k, vt, o, ck, cvt, ik, ivt, rope, ropet, total;
 };
 
 size_t rope_entries(const Dims& d) {
@@ -105,6 +107,8 @@ BlockPlan plan_block(const Dims& d, int Bb, size_t base) {
   }
   p.rope = off;
   off += al(rope_entries(d) * sizeof(float2));
+  p.ropet = off;
+  off += al((size_t)d.L * (d.hd / 2) * sizeof(float2));
   p.total = off;
   return p;
 }
@@ -259,22 +263,27 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
   T* m = reinterpret_cast<T*>(at(ws, p.m));
   T* o = reinterpret_cast<T*>(at(ws, p.o));
   float2* rope = reinterpret_cast<float2*>(at(ws, p.rope));
+  float2* ropet = reinterpret_cast<float2*>(at(ws, p.ropet));
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.hd));
+  const int P = pad256(d.L);  // padded row pitch of the token-row packing GEMMs
 
-  if (!rope_ready) HIP_TRY(launch_rope_table(rope, d.hd, d.F, d.Hh, d.Ww, st));
+  if (!rope_ready) {
+    HIP_TRY(launch_rope_table(rope, d.hd, d.F, d.Hh, d.Ww, st));
+    HIP_TRY(launch_rope_tokens(ropet, rope, d.hd, d.F, d.Hh, d.Ww, st));
+  }
 
   // self-attention sublayer
   HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, mod + 0 * d.D, mod + 1 * d.D, mbs, st); }));
   HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.vt), Bb * d.heads, d.hd, d.L, d.Lp, st));
   {
     GemmArgs g;
-    g.M = M; g.N = 3 * d.D; g.K = d.D;
-    g.A = m; g.lda = d.D; g.a_rpb = M; g.a_bstride = 0;
+    g.M = Bb * P; g.N = 3 * d.D; g.K = d.D;
+    g.A = m; g.lda = d.D; g.a_rpb = P; g.a_bstride = (long long)d.L * d.D; g.a_valid = d.L;
     g.Wt = w->qkv_w; g.ldw = d.D; g.bias = w->qkv_b;
-    g.c_rpb = d.L;
+    g.c_rpb = P; g.c_valid = d.L;
     g.q = at(ws, p.q); g.k = at(ws, p.k); g.vt = at(ws, p.vt);
     g.nq = d.D; g.nk = d.D; g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
-    g.rope = rope; g.gF = d.F; g.gH = d.Hh; g.gW = d.Ww;
+    g.rope = ropet;
     HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
   }
   {
@@ -297,30 +306,32 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
   HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, nullptr, nullptr, 0, st); }));
   {
     GemmArgs g;
-    g.M = M; g.N = d.D; g.K = d.D;
-    g.A = m; g.lda = d.D; g.a_rpb = M;
+    g.M = Bb * P; g.N = d.D; g.K = d.D;
+    g.A = m; g.lda = d.D; g.a_rpb = P; g.a_bstride = (long long)d.L * d.D; g.a_valid = d.L;
     g.Wt = w->cq_w; g.ldw = d.D; g.bias = w->cq_b;
-    g.c_rpb = d.L; g.q = at(ws, p.q); g.nq = d.D; g.nk = 0;
+    g.c_rpb = P; g.c_valid = d.L; g.q = at(ws, p.q); g.nq = d.D; g.nk = 0;
     g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
     HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
   }
   {
     GemmArgs g;
-    g.M = Bb * d.Lt; g.N = 2 * d.D; g.K = d.D;
+    const int Pt = pad256(d.Lt);
+    g.M = Bb * Pt; g.N = 2 * d.D; g.K = d.D;
     g.A = static_cast<const char*>(ctx) + (size_t)d.Li * d.D * d.es;
-    g.lda = d.D; g.a_rpb = d.Lt; g.a_bstride = (long long)d.Lc * d.D;
+    g.lda = d.D; g.a_rpb = Pt; g.a_bstride = (long long)d.Lc * d.D; g.a_valid = d.Lt;
     g.Wt = w->ckv_w; g.ldw = d.D; g.bias = w->ckv_b;
-    g.c_rpb = d.Lt; g.k = at(ws, p.ck); g.vt = at(ws, p.cvt); g.nq = 0; g.nk = d.D;
+    g.c_rpb = Pt; g.c_valid = d.Lt; g.k = at(ws, p.ck); g.vt = at(ws, p.cvt); g.nq = 0; g.nk = d.D;
     g.heads = d.heads; g.hd = d.hd; g.Lp = d.Ltp;
     HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.cvt), Bb * d.heads, d.hd, d.Lt, d.Ltp, st));
     HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
   }
   if (d.Li > 0) {
     GemmArgs g;
-    g.M = Bb * d.Li; g.N = 2 * d.D; g.K = d.D;
-    g.A = ctx; g.lda = d.D; g.a_rpb = d.Li; g.a_bstride = (long long)d.Lc * d.D;
+    const int Pi = pad256(d.Li);
+    g.M = Bb * Pi; g.N = 2 * d.D; g.K = d.D;
+    g.A = ctx; g.lda = d.D; g.a_rpb = Pi; g.a_bstride = (long long)d.Lc * d.D; g.a_valid = d.Li;
     g.Wt = w->ikv_w; g.ldw = d.D; g.bias = w->ikv_b;
-    g.c_rpb = d.Li; g.k = at(ws, p.ik); g.vt = at(ws, p.ivt); g.nq = 0; g.nk = d.D;
+    g.c_rpb = Pi; g.c_valid = d.Li; g.k = at(ws, p.ik); g.vt = at(ws, p.ivt); g.nq = 0; g.nk = d.D;
     g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lip;
     HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.ivt), Bb * d.heads, d.hd, d.Li, d.Lip, st));
     HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));

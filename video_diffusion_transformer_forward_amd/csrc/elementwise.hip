@@ -173,6 +173,29 @@ __global__ void rope_table_kernel(float2* tab, int hd, int F, int Hh, int Ww) {
   tab[idx] = make_float2((float)cos(phi), (float)sin(phi));
 }
 
+// tok[t][j] = the segment-table entry of pair j at token t's grid position
+__global__ void rope_tokens_kernel(float2* __restrict__ tok, const float2* __restrict__ tab, int hd, int F, int Hh,
+                                   int Ww) {
+  const int ds = 2 * (hd / 6);
+  const int df = hd - 2 * ds;
+  const int hp = hd / 2;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long n = (long long)F * Hh * Ww * hp;
+  if (idx >= n) return;
+  const int t = (int)(idx / hp), j = (int)(idx - (long long)t * hp);
+  const int hw = Hh * Ww;
+  const int f = t / hw, rem = t - f * hw;
+  const int yy = rem / Ww, xx = rem - yy * Ww;
+  int k;
+  if (j < df / 2)
+    k = f * (df / 2) + j;
+  else if (j < df / 2 + ds / 2)
+    k = F * (df / 2) + yy * (ds / 2) + (j - df / 2);
+  else
+    k = F * (df / 2) + Hh * (ds / 2) + xx * (ds / 2) + (j - df / 2 - ds / 2);
+  tok[idx] = tab[k];
+}
+
 __device__ __forceinline__ int vt_perm_e(int t) { return (t & ~0xC) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2); }
 
 template <typename T>
@@ -278,6 +301,12 @@ hipError_t launch_rope_table(float2* tab, int hd, int F, int Hh, int Ww, hipStre
   const int df = hd - 2 * ds;
   const int n = F * (df / 2) + Hh * (ds / 2) + Ww * (ds / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, tab, hd, F, Hh, Ww);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_tokens(float2* tok, const float2* tab, int hd, int F, int Hh, int Ww, hipStream_t st) {
+  const long long n = (long long)F * Hh * Ww * (hd / 2);
+  hipLaunchKernelGGL(rope_tokens_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tok, tab, hd, F, Hh, Ww);
   return hipGetLastError();
 }
 

@@ -42,7 +42,11 @@ struct Gemm {
   static constexpr int SW = ((size_t)BM * (BN + 4) * 4 <= PIPE_BYTES) ? BN : BN / WN;
   static constexpr int SWP = SW + 4;
   static constexpr size_t SLAB_BYTES = (size_t)BM * SWP * 4;
-  static constexpr size_t LDS_BYTES = PIPE_BYTES > SLAB_BYTES ? PIPE_BYTES : SLAB_BYTES;
+  // the v^T section of a packing GEMM stages its slab transposed ([column][row])
+  static constexpr int SWPT = BM + 8;
+  static constexpr size_t SLABT_BYTES = EPI == EPI_PACK ? (size_t)SW * SWPT * 4 : 0;
+  static constexpr size_t SLAB_MAX = SLAB_BYTES > SLABT_BYTES ? SLAB_BYTES : SLABT_BYTES;
+  static constexpr size_t LDS_BYTES = PIPE_BYTES > SLAB_MAX ? PIPE_BYTES : SLAB_MAX;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(BN % SW == 0 && SW % 8 == 0, "slab");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -205,7 +209,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     for (int i = 0; i < NA; ++i) {
       const int rt = (wave * NA + i) * RPD + rlow;  // row within the tile
       const int r = min(m0 + rt, g.M - 1);
-      const int bb = r / g.a_rpb, t = r - bb * g.a_rpb;
+      const int bb = r / g.a_rpb;
+      int t = r - bb * g.a_rpb;
+      if (g.a_valid > 0) t = min(t, g.a_valid - 1);  // padding rows of a padded row pitch
       a_src[i] = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda + col_off(rt);
     }
 #pragma unroll
@@ -354,12 +360,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // ---- epilogue.  The fp32 tile goes through LDS in column slabs; phase 2
   // walks a slab in 8-element chunks and writes 16-byte pieces.
   float* slab = reinterpret_cast<float*>(smem_raw);
-  constexpr int SW = C::SW, SWP = C::SWP;
+  constexpr int SW = C::SW, SWP = C::SWP, SWPT = C::SWPT;
+  // v^T tiles of a packing GEMM whose rows lie in one batch item (row pitch a
+  // multiple of BM): the slab is staged transposed, so that a lane reads 8
+  // tokens of one feature column as two 16-byte LDS reads and writes them as
+  // one 16-byte store
+  const bool vt_tile = EPI == EPI_PACK && n0 >= g.nq + g.nk && g.c_rpb % BM == 0;
 #pragma unroll
   for (int s0 = 0; s0 < BN; s0 += SW) {
     // phase 1: the accumulators hold C^T (the weight fragment is the MFMA row
     // operand), so element r of lane l is column 8*(r/4) + 4*g2 + r%4, row l32 of
     // its 32x32 block: four consecutive columns per lane, one 16-byte LDS write
+    // (four 4-byte writes down four columns for a transposed slab)
     if (brow0 + BN / WN > s0 && brow0 < s0 + SW) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -370,8 +382,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
             const int row = arow0 + 32 * i + l32;
-            const f32x4 q4 = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2], acc[i][j][4 * rq + 3]};
-            *reinterpret_cast<f32x4*>(&slab[row * SWP + col]) = q4;
+            if (EPI == EPI_PACK && vt_tile) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) slab[(col + e) * SWPT + row] = acc[i][j][4 * rq + e];
+            } else {
+              const f32x4 q4 = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                                acc[i][j][4 * rq + 3]};
+              *reinterpret_cast<f32x4*>(&slab[row * SWP + col]) = q4;
+            }
           }
         }
       }
@@ -381,7 +399,46 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int nbase = n0 + s0;
     int sec = 0;
     if (EPI == EPI_PACK) sec = nbase < g.nq ? 0 : (nbase < g.nq + g.nk ? 1 : 2);
-    if (EPI == EPI_PACK && sec == 2) {
+    if (EPI == EPI_PACK && vt_tile) {
+      // v^T from the transposed slab.  Lane work item (column, 16-token group,
+      // half hf): tokens 4hf..4hf+3 and 8+4hf..8+4hf+3 of the group, which the
+      // key permutation stores at positions 8hf..8hf+7 -- one 16-byte store;
+      // 32 consecutive items cover 512 contiguous bytes of one v^T row.
+      const int nv0 = nbase - g.nq - g.nk;
+      const int b0 = m0 / g.c_rpb, t0 = m0 - b0 * g.c_rpb;
+      const int valid = g.c_valid > 0 ? g.c_valid : g.c_rpb;
+      constexpr int NG = BM / 16;
+      for (int idx = tid; idx < SW * NG * 2; idx += NT) {
+        const int hf = idx & 1;
+        const int grp = (idx >> 1) % NG;
+        const int col = (idx >> 1) / NG;
+        const float* sp = slab + col * SWPT + 16 * grp + 4 * hf;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 8);
+        const float bn = g.bias[nbase + col];
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[u] = lo[u] + bn;
+          v[4 + u] = hi[u] + bn;
+        }
+        const int nvc = nv0 + col;
+        const int hh = nvc / g.hd, e = nvc - hh * g.hd;
+        T* vrow = reinterpret_cast<T*>(g.vt) + (((long long)b0 * g.heads + hh) * g.hd + e) * g.Lp;
+        const int tb = t0 + 16 * grp;
+        if (tb + 16 <= valid) {
+          Chunk<T> c;
+          pack8(c, v);
+          c.store(vrow + tb + 8 * hf);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int tok = tb + 4 * hf + (u < 4 ? u : u + 4);
+            if (tok < valid) vrow[vt_perm(tok)] = from_f<T>(v[u]);
+          }
+        }
+      }
+    } else if (EPI == EPI_PACK && sec == 2) {
       // v^T: a chunk is 8 consecutive tokens of one feature column
       const int nv0 = nbase - g.nq - g.nk;
       for (int idx = tid; idx < SW * (BM / 8); idx += NT) {
@@ -393,11 +450,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         const int row0 = m0 + r8;
         if (row0 >= g.M) continue;
         const int b0 = row0 / g.c_rpb, t0 = row0 - b0 * g.c_rpb;
+        const int valid = g.c_valid > 0 ? g.c_valid : g.c_rpb;
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = slab[(r8 + u) * SWP + col] + bn;
         T* vrow = reinterpret_cast<T*>(g.vt) + (((long long)b0 * g.heads + hh) * g.hd + e) * g.Lp;
-        if ((t0 & 7) == 0 && t0 + 8 <= g.c_rpb && row0 + 8 <= g.M) {
+        if ((t0 & 7) == 0 && t0 + 8 <= valid && row0 + 8 <= g.M) {
           // 8 aligned tokens: two runs of 4 that stay contiguous under the key permutation
 #pragma unroll
           for (int u = 0; u < 8; ++u) vrow[vt_perm(t0 + u)] = from_f<T>(v[u]);
@@ -407,6 +465,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             const int rr = row0 + u;
             if (rr >= g.M) break;
             const int b = rr / g.c_rpb, t = rr - b * g.c_rpb;
+            if (t >= valid) continue;
             reinterpret_cast<T*>(g.vt)[(((long long)b * g.heads + hh) * g.hd + e) * g.Lp + vt_perm(t)] =
                 from_f<T>(v[u]);
           }
@@ -476,27 +535,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           const int nsec = n - (sec == 0 ? 0 : g.nq);
           const int hh = nsec / g.hd, e0 = nsec - hh * g.hd;
           const int b = row / g.c_rpb, t = row - b * g.c_rpb;
+          if (g.c_valid > 0 && t >= g.c_valid) continue;  // padding row
           if (g.rope) {
-            const int hw = g.gH * g.gW;
-            const int f = t / hw;
-            const int rem = t - f * hw;
-            const int yy = rem / g.gW;
-            const int xx = rem - yy * g.gW;
-            const int ds = 2 * (g.hd / 6);
-            const int df = g.hd - 2 * ds;
+            // per-token (cos, sin) of the four pairs (e0, e0+1) .. (e0+6, e0+7)
+            const f32x4* rp = reinterpret_cast<const f32x4*>(g.rope + (long long)t * (g.hd / 2) + e0 / 2);
+            const f32x4 c01 = rp[0], c23 = rp[1];
+            const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
 #pragma unroll
             for (int u = 0; u < 8; u += 2) {
-              const int e = e0 + u;
-              float2 cs;
-              if (e < df)
-                cs = g.rope[f * (df / 2) + e / 2];
-              else if (e < df + ds)
-                cs = g.rope[g.gF * (df / 2) + yy * (ds / 2) + (e - df) / 2];
-              else
-                cs = g.rope[g.gF * (df / 2) + g.gH * (ds / 2) + xx * (ds / 2) + (e - df - ds) / 2];
               const float u0 = v[u], u1 = v[u + 1];
-              v[u] = u0 * cs.x - u1 * cs.y;
-              v[u + 1] = u0 * cs.y + u1 * cs.x;
+              v[u] = u0 * cs[u] - u1 * cs[u + 1];
+              v[u + 1] = u0 * cs[u + 1] + u1 * cs[u];
             }
           }
           Chunk<T> c;

@@ -12,10 +12,12 @@ enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_STORE_F32 = 2, EPI_RESID = 3, 
 // C[M][N] = A[M][K] * W[N][K]^T + bias, with an epilogue selected by `epi`.
 struct GemmArgs {
   int M = 0, N = 0, K = 0;
-  // A operand (LOAD_PLAIN): row r lives at A + (r / a_rpb) * a_bstride + (r % a_rpb) * lda
+  // A operand (LOAD_PLAIN): row r lives at A + (r / a_rpb) * a_bstride + (r % a_rpb) * lda;
+  // with a_valid > 0, rows r % a_rpb >= a_valid (padding of a padded row pitch) read row a_valid-1
   const void* A = nullptr;
   long long lda = 0, a_bstride = 0;
   int a_rpb = 1;
+  int a_valid = 0;
   // A operand (LOAD_PATCH): (1,2,2) patches of [z ; cond], token rows of `zb_count` videos
   const float* z = nullptr;
   const float* cond = nullptr;
@@ -25,8 +27,10 @@ struct GemmArgs {
   const void* Wt = nullptr;
   long long ldw = 0;
   const float* bias = nullptr;
-  // rows of C belong to batch b = r / c_rpb, token t = r % c_rpb
+  // rows of C belong to batch b = r / c_rpb, token t = r % c_rpb; with c_valid > 0
+  // (EPI_PACK only) tokens t >= c_valid are padding and not stored
   int c_rpb = 1;
+  int c_valid = 0;
   // EPI_STORE*: C + r * ldc + n
   void* C = nullptr;
   long long ldc = 0;
@@ -41,8 +45,7 @@ struct GemmArgs {
   void* vt = nullptr;
   int nq = 0, nk = 0;
   int heads = 1, hd = 128, Lp = 64;
-  const float2* rope = nullptr;  // (cos, sin) table or NULL for no rotation
-  int gF = 1, gH = 1, gW = 1;    // RoPE grid (frames, rows, cols)
+  const float2* rope = nullptr;  // per-token (cos, sin) table [token][hd/2], or NULL for no rotation
 };
 
 template <typename T> hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st);
@@ -69,8 +72,11 @@ template <typename T>
 hipError_t launch_ln_mod(const float* x, void* out, int rows, int D, int rows_per_batch, const float* shift,
                          const float* scale, long long mod_bstride, hipStream_t st);
 
-// (cos, sin) RoPE table for head dim hd over grid (F, Hh, Ww), computed in double.
+// (cos, sin) RoPE table for head dim hd over grid (F, Hh, Ww), computed in double: the
+// frame segment, then the row and column segments, one entry per (position, pair).
 hipError_t launch_rope_table(float2* tab, int hd, int F, int Hh, int Ww, hipStream_t st);
+// Per-token table [F*Hh*Ww][hd/2] gathered from the segment table above.
+hipError_t launch_rope_tokens(float2* tok, const float2* tab, int hd, int F, int Hh, int Ww, hipStream_t st);
 
 // zero the key padding [L, Lp) of a v^T buffer [BH][hd][Lp]
 template <typename T> hipError_t launch_zero_vt_pad(void* vt, int BH, int hd, int L, int Lp, hipStream_t st);
