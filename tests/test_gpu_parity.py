@@ -180,6 +180,24 @@ def test_block_wan13b_full_size_sampled_rows():
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["wan14b_720p_block", "wan14b_i2v_block"])
+def test_block_14b_full_size_sampled_rows(name):
+    """The 14B block at full size: 720p x 81 frames (L = 75600, 40 heads of 128) and I2V at
+    480p (L = 32760, context of 257 image + 512 text tokens, two-source cross-attention):
+    sampled token rows against the oracle, whose keys and values cover every token."""
+    cfg = S.get_config(name)
+    announce(f"block {name} full size")
+    w, x, mod, ctx = block_case(cfg)
+    got = gpu_block(cfg, w, x, mod, ctx)
+    assert np.all(np.isfinite(got))
+    rows = sample_rows(cfg.seq_len, 12, seed=4)
+    ref = oracle_block(cfg, w, x, mod, ctx, rows=rows)
+    err = inc_err(got[:, rows], ref, x[:, rows])
+    print(f"{name} sampled rows: rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------------------- head
 @pytest.mark.parametrize("name", ["toy", "mid_bf16"])
 def test_head(name):
