@@ -571,38 +571,99 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   att_barrier_lds();  // K stage 0 is refilled by the first iteration
 
   // One iteration, entered with the scores S(t) of tile t in S and the
-  // probabilities of its first 32 keys in pf[.][0..1]:
-  //   S(t+1) for keys 0..31 (MFMA)   | probabilities of tile t, keys 32..63 (VALU)
-  //   S(t+1) for keys 32..63 (MFMA)  |
-  //   O += P V, tile t keys 0..31    | masking and row maxima of S(t+1)
-  //   O += P V, tile t keys 32..63   | probabilities of tile t+1, keys 0..31
+  // probabilities of its first 32 keys in pf[.][0..1].  The 32 MFMAs of a
+  // (single query block) wave run as 32 slots, each issuing the LDS read of the
+  // operand needed 8 slots later and a share of the VALU work:
+  //   slots  0..7   S(t+1), keys 0..31    | probabilities of tile t, keys 32..63
+  //   slots  8..15  S(t+1), keys 32..63   | masking and row maxima of S(t+1), keys 0..31
+  //   slots 16..23  O += P V, keys 0..31  | masking and row maxima, keys 32..63; new max
+  //   slots 24..31  O += P V, keys 32..63 | probabilities of tile t+1, keys 0..31
   // K_{t+1} sits in K stage (t+1)%NR, V_t in V stage t%NR.  The loads issued here
   // refill the stages read in the previous iteration: K_{t+NR} and V_{t+NR-1}
   // (indices clamped at the last tile; those copies are never read).  Past the
   // last tile S(n) is computed from a stale stage but masked out entirely.
   // `ph` = t % NR, a literal after inlining, so every LDS offset is an immediate.
+  // A scheduling barrier closes every slot; values consumed in a later slot are
+  // pinned where they are produced.
+  static_assert(QB == 1, "slot schedule for one query block per wave");
   auto iter = [&](int t, int ph) {
     const int kst = (ph + 1) % NR, vst = ph;
     issue_k(min(t + NR, n - 1), ph);
     issue_v(min(t + NR - 1, n - 1), (ph + NR - 1) % NR);
-    // the scheduler may interleave inside a phase, never across (that would take
-    // a second set of score registers)
-    scores(S, kst, 0);
-    probs(S, 1, pf);
-    pin_probs(1);
-    __builtin_amdgcn_sched_barrier(0);
-    scores(S, kst, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mask(S, t + 1);
-    pv(vst, 0, pf);
-    rowmax(S, mx);
-    const bool moved = new_max(mx);
-    pin_stats();
-    __builtin_amdgcn_sched_barrier(0);
-    pv(vst, 2, pf);
-    probs(S, 0, pf);
-    pin_probs(0);
-    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* kbase = smem_raw + kst * Cfg::KT_B;
+    const unsigned char* vbase = smem_raw + VRING + vst * Cfg::VT_B;
+    // operand of slot i: K block i/8 step i%8, then V^T 16-key step (i-16)/4, d block (i-16)%4
+    auto raddr = [&](int i) -> const unsigned char* {
+      if (i < 16) return kbase + (i / 8) * KBLK_B + koff[i % 8];
+      return vbase + ((i - 16) % 4) * VBLK_B + voff[(i - 16) / 4];
+    };
+    constexpr int AHEAD = 8;
+    Chunk<T> rf[32];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) rf[i].load(raddr(i));
+    const bool mask_next = (t + 2) * ATT_BN > Lk;
+    float nmc = -m[0] * c;
+    float vmax = -INFINITY;
+    float pbuf[8];
+    bool moved = false;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + AHEAD < 32) rf[i + AHEAD].load(raddr(i + AHEAD));
+      if (i < 16) {
+        const int kb = i / 8, st = i % 8;
+        if (st == 0) {
+          const f32x16 zero = {};
+          S[0][kb] = zero;
+        }
+        mma32(S[0][kb], rf[i], qf[0][st]);
+      } else {
+        const int u = (i - 16) / 4, db = (i - 16) % 4;
+        mma32(o[0][db], rf[i], pf[0][u]);
+      }
+      if (i < 8) {
+        // probabilities of tile t, keys 32..63: elements 2i, 2i+1 of S(t) block 1
+#pragma unroll
+        for (int e = 2 * i; e < 2 * i + 2; ++e) {
+          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][1][e], c, nmc));
+          l[0] += pbuf[e % 8];
+        }
+        if (i % 4 == 3) {
+          pack8(pf[0][2 + i / 4], pbuf);
+          asm volatile("" : "+v"(pf[0][2 + i / 4].v), "+v"(l[0]));
+        }
+      } else if (i < 24) {
+        // row maxima of S(t+1): block 0 in slots 8..15, block 1 in slots 16..23
+        const int kb = (i - 8) / 8, k = (i - 8) % 8;
+        if (k == 0 && mask_next) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = (t + 1) * ATT_BN + 32 * kb + 8 * (r / 4) + 4 * g2 + (r % 4);
+            if (key >= Lk) S[0][kb][r] = -INFINITY;
+          }
+        }
+        vmax = __builtin_elementwise_maximum(vmax, __builtin_elementwise_maximum(S[0][kb][2 * k], S[0][kb][2 * k + 1]));
+        asm volatile("" : "+v"(vmax));
+        if (i == 23) {
+          mx[0] = __builtin_elementwise_maximum(vmax, __shfl_xor(vmax, 32, 64));
+          moved = new_max(mx);
+          nmc = -m[0] * c;
+          pin_stats();
+          asm volatile("" : "+v"(nmc));
+        }
+      } else {
+        // probabilities of tile t+1, keys 0..31: elements 2(i-24), +1 of S(t+1) block 0
+#pragma unroll
+        for (int e = 2 * (i - 24); e < 2 * (i - 24) + 2; ++e) {
+          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][0][e], c, nmc));
+          l[0] += pbuf[e % 8];
+        }
+        if (i % 4 == 3) {
+          pack8(pf[0][(i - 24) / 4], pbuf);
+          asm volatile("" : "+v"(pf[0][(i - 24) / 4].v), "+v"(l[0]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (moved) scale_o();
     att_wait_vmcnt<INFLIGHT>();  // K_{t+2} and V_{t+1} have landed
     att_barrier_lds();
