@@ -571,9 +571,9 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   att_barrier_lds();  // K stage 0 is refilled by the first iteration
 
   // One iteration, entered with the scores S(t) of tile t in S and the
-  // probabilities of its first 32 keys in pf[.][0..1].  The 32 MFMAs of a
-  // (single query block) wave run as 32 slots, each issuing the LDS read of the
-  // operand needed 8 slots later and a share of the VALU work:
+  // probabilities of its first 32 keys in pf[.][0..1].  The MFMAs of a
+  // wave run as 32 slots (QB MFMAs each, one per query block), each issuing the
+  // LDS read of the operand needed 8 slots later and a share of the VALU work:
   //   slots  0..7   S(t+1), keys 0..31    | probabilities of tile t, keys 32..63
   //   slots  8..15  S(t+1), keys 32..63   | masking and row maxima of S(t+1), keys 0..31
   //   slots 16..23  O += P V, keys 0..31  | masking and row maxima, keys 32..63; new max
@@ -585,7 +585,6 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   // `ph` = t % NR, a literal after inlining, so every LDS offset is an immediate.
   // A scheduling barrier closes every slot; values consumed in a later slot are
   // pinned where they are produced.
-  static_assert(QB == 1, "slot schedule for one query block per wave");
   auto iter = [&](int t, int ph) {
     const int kst = (ph + 1) % NR, vst = ph;
     issue_k(min(t + NR, n - 1), ph);
@@ -602,64 +601,86 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) rf[i].load(raddr(i));
     const bool mask_next = (t + 2) * ATT_BN > Lk;
-    float nmc = -m[0] * c;
-    float vmax = -INFINITY;
-    float pbuf[8];
+    float nmc[QB], vmax[QB], pbuf[QB][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      nmc[qb] = -m[qb] * c;
+      vmax[qb] = -INFINITY;
+    }
     bool moved = false;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (i + AHEAD < 32) rf[i + AHEAD].load(raddr(i + AHEAD));
-      if (i < 16) {
-        const int kb = i / 8, st = i % 8;
-        if (st == 0) {
-          const f32x16 zero = {};
-          S[0][kb] = zero;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (i < 16) {
+          const int kb = i / 8, st = i % 8;
+          if (st == 0) {
+            const f32x16 zero = {};
+            S[qb][kb] = zero;
+          }
+          mma32(S[qb][kb], rf[i], qf[qb][st]);
+        } else {
+          const int u = (i - 16) / 4, db = (i - 16) % 4;
+          mma32(o[qb][db], rf[i], pf[qb][u]);
         }
-        mma32(S[0][kb], rf[i], qf[0][st]);
-      } else {
-        const int u = (i - 16) / 4, db = (i - 16) % 4;
-        mma32(o[0][db], rf[i], pf[0][u]);
       }
       if (i < 8) {
         // probabilities of tile t, keys 32..63: elements 2i, 2i+1 of S(t) block 1
 #pragma unroll
-        for (int e = 2 * i; e < 2 * i + 2; ++e) {
-          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][1][e], c, nmc));
-          l[0] += pbuf[e % 8];
-        }
-        if (i % 4 == 3) {
-          pack8(pf[0][2 + i / 4], pbuf);
-          asm volatile("" : "+v"(pf[0][2 + i / 4].v), "+v"(l[0]));
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int e = 2 * i; e < 2 * i + 2; ++e) {
+            pbuf[qb][e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][1][e], c, nmc[qb]));
+            l[qb] += pbuf[qb][e % 8];
+          }
+          if (i % 4 == 3) {
+            pack8(pf[qb][2 + i / 4], pbuf[qb]);
+            asm volatile("" : "+v"(pf[qb][2 + i / 4].v), "+v"(l[qb]));
+          }
         }
       } else if (i < 24) {
         // row maxima of S(t+1): block 0 in slots 8..15, block 1 in slots 16..23
         const int kb = (i - 8) / 8, k = (i - 8) % 8;
         if (k == 0 && mask_next) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = (t + 1) * ATT_BN + 32 * kb + 8 * (r / 4) + 4 * g2 + (r % 4);
-            if (key >= Lk) S[0][kb][r] = -INFINITY;
-          }
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = (t + 1) * ATT_BN + 32 * kb + 8 * (r / 4) + 4 * g2 + (r % 4);
+              if (key >= Lk) S[qb][kb][r] = -INFINITY;
+            }
         }
-        vmax = __builtin_elementwise_maximum(vmax, __builtin_elementwise_maximum(S[0][kb][2 * k], S[0][kb][2 * k + 1]));
-        asm volatile("" : "+v"(vmax));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          vmax[qb] = __builtin_elementwise_maximum(
+              vmax[qb], __builtin_elementwise_maximum(S[qb][kb][2 * k], S[qb][kb][2 * k + 1]));
+          asm volatile("" : "+v"(vmax[qb]));
+        }
         if (i == 23) {
-          mx[0] = __builtin_elementwise_maximum(vmax, __shfl_xor(vmax, 32, 64));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) mx[qb] = __builtin_elementwise_maximum(vmax[qb], __shfl_xor(vmax[qb], 32, 64));
           moved = new_max(mx);
-          nmc = -m[0] * c;
           pin_stats();
-          asm volatile("" : "+v"(nmc));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            nmc[qb] = -m[qb] * c;
+            asm volatile("" : "+v"(nmc[qb]));
+          }
         }
       } else {
         // probabilities of tile t+1, keys 0..31: elements 2(i-24), +1 of S(t+1) block 0
 #pragma unroll
-        for (int e = 2 * (i - 24); e < 2 * (i - 24) + 2; ++e) {
-          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][0][e], c, nmc));
-          l[0] += pbuf[e % 8];
-        }
-        if (i % 4 == 3) {
-          pack8(pf[0][(i - 24) / 4], pbuf);
-          asm volatile("" : "+v"(pf[0][(i - 24) / 4].v), "+v"(l[0]));
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int e = 2 * (i - 24); e < 2 * (i - 24) + 2; ++e) {
+            pbuf[qb][e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][0][e], c, nmc[qb]));
+            l[qb] += pbuf[qb][e % 8];
+          }
+          if (i % 4 == 3) {
+            pack8(pf[qb][(i - 24) / 4], pbuf[qb]);
+            asm volatile("" : "+v"(pf[qb][(i - 24) / 4].v), "+v"(l[qb]));
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
