@@ -226,14 +226,20 @@ def _lin(x, w, b):
     return f64(x) @ f64(w).T + f64(b)
 
 
-def self_attention(m_all, w, heads, grid, rows=None):
+def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None):
     """Self-attention sublayer output (before its gate).
 
     q, k, v = m W_qkv^T + b_qkv (rows of W_qkv ordered [q; k; v]); RoPE on q and
     k ([P3] core code); full attention over every token; output projection W_o.
     m_all: the modulated input of every token (source of keys and values);
     rows: token indices whose outputs are wanted (None = all).
+    attn: a cached attention output (B, L, D) (heads concatenated, before W_o)
+    used instead of computing q, k, v and the attention (the diffusion cache);
+    record: a list that receives the attention output computed here.
     """
+    if attn is not None:
+        a = f64(attn) if rows is None else f64(attn)[:, rows]
+        return _lin(a, w["o_w"], w["o_b"])
     B, L, D = m_all.shape
     d = D // heads
     wq, wk, wv = np.split(f64(w["qkv_w"]), 3, axis=0)
@@ -244,6 +250,8 @@ def self_attention(m_all, w, heads, grid, rows=None):
     n = mq.shape[1]
     q = rope_apply(_lin(mq, wq, bq).reshape(B, n, heads, d), grid, rows).reshape(B, n, D)
     a = multihead_attention(q, k, v, heads)
+    if record is not None:
+        record.append(a)
     return _lin(a, w["o_w"], w["o_b"])
 
 
@@ -274,7 +282,7 @@ def ffn(xm, w):
     return _lin(gelu(_lin(xm, w["ff1_w"], w["ff1_b"])), w["ff2_w"], w["ff2_b"])
 
 
-def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None):
+def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, record=None):
     """One DiT block, residual stream in float64.
 
         x <- x + g1 * SA(LN(x) (1 + sc1) + sh1)
@@ -285,6 +293,7 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None):
     scale2, gate2); ctx: (B, L_img + L_txt, D).
     rows: if given, return only those tokens' outputs (the keys and values of
     self-attention still come from every token) -> (B, len(rows), D).
+    attn / record: see self_attention (diffusion cache).
     """
     x = f64(x)
     mod = f64(mod)
@@ -293,7 +302,7 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None):
     sh1, sc1, g1, sh2, sc2, g2 = [mod[:, i][:, None, :] for i in range(6)]
     m_all = modulate(layer_norm(x), sh1, sc1)
     xr = x if rows is None else x[:, rows]
-    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows)
+    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record)
     xr = xr + cross_attention(layer_norm(xr), ctx, w, heads, img_len)
     xr = xr + g2 * ffn(modulate(layer_norm(xr), sh2, sc2), w)
     return xr
@@ -321,15 +330,20 @@ def euler_update(z, v, dt):
     return f64(z) + dt * f64(v)
 
 
-def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0):
-    """Velocity prediction of the whole DiT for one context: (B, 16, F, H, W)."""
+def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0, attn_cache=None, record=None):
+    """Velocity prediction of the whole DiT for one context: (B, 16, F, H, W).
+
+    attn_cache: per-block cached self-attention outputs to use instead of
+    computing them; record: a list that receives each block's attention output.
+    """
     B, _, F, H, W = np.shape(z)
     grid = (F, H // 2, W // 2)
     x = patchify(z, cond, model_w["pe_w"], model_w["pe_b"])
     mod = time_modulation(tau, model_w["t1_w"], model_w["t1_b"], model_w["t2_w"],
                           model_w["t2_b"], model_w["m_w"], model_w["m_b"])
-    for w in blocks_w:
-        x = dit_block(x, mod, ctx, w, heads, grid, img_len)
+    for i, w in enumerate(blocks_w):
+        x = dit_block(x, mod, ctx, w, heads, grid, img_len,
+                      attn=None if attn_cache is None else attn_cache[i], record=record)
     p = head(x, model_w["hd_w"], model_w["hd_b"])
     return patch_scatter(p, F, H, W)
 
@@ -339,4 +353,45 @@ def denoise_step(z, cond, ctx_cond, ctx_null, model_w, blocks_w, heads, tau, dt,
     """One CFG denoise step: both branches, guidance combine, Euler update."""
     v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len)
     v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len)
+    return euler_update(z, cfg_combine(v_c, v_u, guide_scale), dt)
+
+
+# --------------------------------------------------------------------------- diffusion cache
+CACHE_STORE = 1
+CACHE_REUSE_ATTN = 2
+CACHE_REUSE_UNCOND = 4
+
+
+def denoise_step_cached(z, cond, ctx_cond, ctx_null, model_w, blocks_w, heads, tau, dt,
+                        guide_scale, mode, cache, img_len=0):
+    """One CFG denoise step with the diffusion cache ([P2] method: inference reuses
+    the similarity of attention between sampling steps and of the two CFG
+    branches; the pages give no further rule, the reading taken is):
+
+      CACHE_STORE         the full step; keeps every block's self-attention output
+                          of both branches and the unconditional velocity;
+      CACHE_REUSE_ATTN    every block takes its self-attention output (before the
+                          output projection) from the cache instead of computing it;
+      CACHE_REUSE_UNCOND  only the conditional branch runs; the unconditional
+                          velocity comes from the cache.
+
+    cache: a dict filled by a CACHE_STORE step ("attn_c", "attn_u": per-block
+    arrays; "v_u": the unconditional velocity).  Returns the new latent.
+    """
+    if mode == CACHE_STORE:
+        rec_c, rec_u = [], []
+        v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len, record=rec_c)
+        v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len, record=rec_u)
+        cache["attn_c"], cache["attn_u"], cache["v_u"] = rec_c, rec_u, v_u
+    else:
+        if mode & ~(CACHE_REUSE_ATTN | CACHE_REUSE_UNCOND) or mode == 0:
+            raise ValueError(f"cache mode {mode}")
+        reuse_attn = bool(mode & CACHE_REUSE_ATTN)
+        v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len,
+                          attn_cache=cache["attn_c"] if reuse_attn else None)
+        if mode & CACHE_REUSE_UNCOND:
+            v_u = cache["v_u"]
+        else:
+            v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len,
+                              attn_cache=cache["attn_u"] if reuse_attn else None)
     return euler_update(z, cfg_combine(v_c, v_u, guide_scale), dt)

@@ -461,3 +461,70 @@ def test_step_guidance_linearity():
     # g = 1 is the conditional branch alone
     v_c = O.dit_forward(z, None, ctx_c, mw, blocks, H, 250.0)
     np.testing.assert_allclose(zs[1.0], z + 0.05 * v_c, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- diffusion cache
+def _cache_case(seed_shift=0):
+    D, H = 24, 2
+    z = rng.standard_normal((1, 16, 2, 4, 6))
+    mw = _tiny_model(D, 16, False)
+    blocks = [_tiny_weights(D, 32, False) for _ in range(2)]
+    ctx_c, ctx_n = rng.standard_normal((1, 5, D)), rng.standard_normal((1, 5, D))
+    return D, H, z, mw, blocks, ctx_c, ctx_n
+
+
+def test_cache_store_is_the_plain_step():
+    D, H, z, mw, blocks, ctx_c, ctx_n = _cache_case()
+    cache = {}
+    a = O.denoise_step_cached(z, None, ctx_c, ctx_n, mw, blocks, H, 400.0, 0.05, 5.0, O.CACHE_STORE, cache)
+    b = O.denoise_step(z, None, ctx_c, ctx_n, mw, blocks, H, 400.0, 0.05, 5.0)
+    np.testing.assert_array_equal(a, b)
+    L = 2 * 2 * 3
+    assert len(cache["attn_c"]) == 2 and len(cache["attn_u"]) == 2
+    assert all(c.shape == (1, L, D) for c in cache["attn_c"] + cache["attn_u"])
+    assert cache["v_u"].shape == z.shape
+
+
+@pytest.mark.parametrize("mode", [O.CACHE_REUSE_ATTN, O.CACHE_REUSE_UNCOND,
+                                  O.CACHE_REUSE_ATTN | O.CACHE_REUSE_UNCOND])
+def test_cache_reuse_at_the_stored_state_reproduces_the_step(mode):
+    D, H, z, mw, blocks, ctx_c, ctx_n = _cache_case()
+    cache = {}
+    a = O.denoise_step_cached(z, None, ctx_c, ctx_n, mw, blocks, H, 400.0, 0.05, 5.0, O.CACHE_STORE, cache)
+    b = O.denoise_step_cached(z, None, ctx_c, ctx_n, mw, blocks, H, 400.0, 0.05, 5.0, mode, cache)
+    np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-13)
+
+
+def test_cache_reuse_attn_skips_the_attention():
+    D, H, z, mw, blocks, ctx_c, ctx_n = _cache_case()
+    cache = {}
+    O.denoise_step_cached(z, None, ctx_c, ctx_n, mw, blocks, H, 400.0, 0.05, 5.0, O.CACHE_STORE, cache)
+    z2 = z + 0.3 * rng.standard_normal(z.shape)
+    r1 = O.denoise_step_cached(z2, None, ctx_c, ctx_n, mw, blocks, H, 350.0, 0.05, 5.0, O.CACHE_REUSE_ATTN, cache)
+    plain = O.denoise_step(z2, None, ctx_c, ctx_n, mw, blocks, H, 350.0, 0.05, 5.0)
+    assert np.abs(r1 - plain).max() > 1e-6          # a stale cache changes the result
+    # the q/k/v projection is not used when the attention comes from the cache
+    blocks_q = [dict(w, qkv_w=w["qkv_w"] * 3.0 + 1.0) for w in blocks]
+    r2 = O.denoise_step_cached(z2, None, ctx_c, ctx_n, mw, blocks_q, H, 350.0, 0.05, 5.0, O.CACHE_REUSE_ATTN, cache)
+    np.testing.assert_array_equal(r1, r2)
+    # with the output projection zeroed the self-attention contributes nothing, cached or not
+    blocks_0 = [dict(w, o_w=np.zeros_like(w["o_w"]), o_b=np.zeros_like(w["o_b"])) for w in blocks]
+    r3 = O.denoise_step_cached(z2, None, ctx_c, ctx_n, mw, blocks_0, H, 350.0, 0.05, 5.0, O.CACHE_REUSE_ATTN, cache)
+    p3 = O.denoise_step(z2, None, ctx_c, ctx_n, mw, blocks_0, H, 350.0, 0.05, 5.0)
+    np.testing.assert_allclose(r3, p3, rtol=1e-12, atol=1e-13)
+
+
+def test_cache_reuse_uncond_guidance_limits():
+    D, H, z, mw, blocks, ctx_c, ctx_n = _cache_case()
+    cache = {}
+    O.denoise_step_cached(z, None, ctx_c, ctx_n, mw, blocks, H, 400.0, 0.05, 5.0, O.CACHE_STORE, cache)
+    z2 = z + 0.3 * rng.standard_normal(z.shape)
+    # g = 1: the conditional branch alone, whatever the cache holds
+    a = O.denoise_step_cached(z2, None, ctx_c, ctx_n, mw, blocks, H, 350.0, 0.05, 1.0, O.CACHE_REUSE_UNCOND, cache)
+    b = O.denoise_step(z2, None, ctx_c, ctx_n, mw, blocks, H, 350.0, 0.05, 1.0)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    # g = 0: the cached unconditional velocity alone
+    c = O.denoise_step_cached(z2, None, ctx_c, ctx_n, mw, blocks, H, 350.0, 0.05, 0.0, O.CACHE_REUSE_UNCOND, cache)
+    np.testing.assert_allclose(c, z2 + 0.05 * cache["v_u"], rtol=1e-12, atol=1e-13)
+    with pytest.raises(ValueError):
+        O.denoise_step_cached(z2, None, ctx_c, ctx_n, mw, blocks, H, 350.0, 0.05, 1.0, 8, cache)
