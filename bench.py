@@ -124,6 +124,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="wan13b_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-modes", action="store_true", help="skip timing the diffusion-cache step modes")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB -> 1 GiB elementwise copy three times: the "
                          "known-size kernel that scales the HBM byte counters of a counter-collection run")
@@ -176,6 +177,29 @@ def main():
                                            ("cross_attention", N.KERNEL_CROSS_ATTENTION),
                                            ("gemm", N.KERNEL_GEMM), ("elementwise", N.KERNEL_ELEMENTWISE))}
     assert bool(torch.isfinite(z).all())
+    # diffusion cache: one step in each mode (after a store step), timed alone
+    cache_ms = None
+    if not args.no_cache_modes:
+        cache = W.diffusion_cache(cfg, cfg.n_blocks)
+        modes = {"store": N.CACHE_STORE, "reuse_attn": N.CACHE_REUSE_ATTN, "reuse_uncond": N.CACHE_REUSE_UNCOND,
+                 "reuse_attn_uncond": N.CACHE_REUSE_ATTN | N.CACHE_REUSE_UNCOND}
+        zc = z0.clone()
+        W.denoise_step_cached(cfg, model, zc, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale,
+                              N.CACHE_STORE, cache, ws)
+        cache_ms = {}
+        for name, mode in modes.items():
+            W.denoise_step_cached(cfg, model, zc, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale,
+                                  mode, cache, ws)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(2):
+                W.denoise_step_cached(cfg, model, zc, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale,
+                                      mode, cache, ws)
+            torch.cuda.synchronize()
+            cache_ms[name] = round((time.perf_counter() - t1) / 2 * 1e3, 3)
+        cache_gb = round(cache.numel() / 1e9, 3)
+        del cache
+        torch.cuda.empty_cache()
     if args.calib_copy:
         src = torch.ones(CALIB_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -225,6 +249,11 @@ def main():
                      "avg_launch_ms": round(attn_avg, 4), "launches": attn_n,
                      "flop_per_launch": bf["self_attention"]},
     }
+    if cache_ms is not None:
+        out["diffusion_cache"] = {
+            "ms_per_step": cache_ms, "cache_gb": cache_gb,
+            "note": "one CFG step per mode after a store step; a reuse step skips the QKV projection and "
+                    "self-attention (reuse_attn) and/or the unconditional branch (reuse_uncond)"}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)

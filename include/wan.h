@@ -180,6 +180,35 @@ int wan_denoise_step(const wan_shape* s, const wan_model_weights* w, float* z, c
                      float guide_scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Diffusion cache ([P2] method: inference exploits the similarity of attention
+ * between sampling steps and of the two CFG branches; [P2] experiments: 1.62x).
+ * One step as wan_denoise_step, under one of these modes:
+ *   WAN_CACHE_STORE         the full step; also writes every block's self-attention
+ *                           output of both branches (before the output projection)
+ *                           and the unconditional head output into `cache`;
+ *   WAN_CACHE_REUSE_ATTN    every block takes its self-attention output from the
+ *                           cache: the q/k/v projection and the attention are skipped;
+ *   WAN_CACHE_REUSE_UNCOND  only the conditional branch runs (batch B instead of 2B);
+ *                           the unconditional head output comes from the cache.
+ * The two REUSE flags combine.  A REUSE step reads what the last STORE step on
+ * the same shape and cache wrote; the cache is not checked for that (a REUSE
+ * step on a cache no STORE step has filled reads undefined values).
+ * cache: caller-owned device memory of wan_cache_bytes(s) bytes, laid out as
+ *   n_blocks x (2B, L, D) attention outputs in the mode's type (conditional
+ *   batch items first), then (B, L, out_ch*4) float32 unconditional head output.
+ * Returns WAN_E_MODE for any other mode value, WAN_E_WORKSPACE when cache_bytes
+ * is below wan_cache_bytes(s); otherwise as wan_denoise_step.
+ */
+#define WAN_CACHE_STORE 1
+#define WAN_CACHE_REUSE_ATTN 2
+#define WAN_CACHE_REUSE_UNCOND 4
+size_t wan_cache_bytes(const wan_shape* s, int n_blocks, int* status);
+int wan_denoise_step_cached(const wan_shape* s, const wan_model_weights* w, float* z, const float* cond,
+                            const void* ctx_cond, const void* ctx_null, float timestep, float dt,
+                            float guide_scale, int cache_mode, void* cache, size_t cache_bytes,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing (measurement support, not part of the computation).
  * While enabled, the library brackets every launch of the kernel classes below
  * with a pair of hipEvents recorded on the launch stream.  wan_timing_read

@@ -124,6 +124,31 @@ def test_step_argument_errors():
     assert call() == N.WAN_E_NULL
 
 
+def test_cache_sizes_and_argument_errors():
+    lib = N.load()
+    cfg = get_config("toy_step")
+    sh = shape_of(cfg)
+    st = ctypes.c_int(0)
+    one = lib.wan_cache_bytes(ctypes.byref(sh), 1, ctypes.byref(st))
+    assert st.value == N.WAN_OK and one > 0
+    # n_blocks attention slots (2B, L, D) in the mode's type, then (B, L, 64) float32
+    L, D = cfg.seq_len, cfg.dim
+    slot = 2 * cfg.batch * L * D * 4
+    assert lib.wan_cache_bytes(ctypes.byref(sh), 3, ctypes.byref(st)) - one >= 2 * slot
+    assert lib.wan_cache_bytes(ctypes.byref(sh), 0, ctypes.byref(st)) == 0 and st.value == N.WAN_E_SHAPE
+    blocks = (N.WanBlockWeights * 2)(N.WanBlockWeights(*([FAKE] * 16)), N.WanBlockWeights(*([FAKE] * 16)))
+    mw = N.WanModelWeights(*([FAKE] * 10), 2, ctypes.cast(blocks, ctypes.POINTER(N.WanBlockWeights)))
+    need = lib.wan_cache_bytes(ctypes.byref(sh), 2, ctypes.byref(st))
+    call = lambda mode=N.CACHE_STORE, cache=FAKE, cb=need: lib.wan_denoise_step_cached(
+        ctypes.byref(sh), ctypes.byref(mw), FAKE, None, FAKE, FAKE, 500.0, 0.05, 5.0, mode, cache, cb, FAKE,
+        1 << 40, None)
+    for bad in (0, 3, 5, 7, 8, -1):
+        assert call(mode=bad) == N.WAN_E_MODE
+    assert call(cache=None) == N.WAN_E_NULL
+    assert call(cache=FAKE + 4) == N.WAN_E_ALIGN
+    assert call(cb=need - 1) == N.WAN_E_WORKSPACE
+
+
 def test_no_device_reported_as_hip_error():
     """With valid arguments the first HIP query fails on a host without a gfx950 GPU."""
     try:

@@ -319,3 +319,71 @@ def test_step_wan13b_30_blocks_properties():
     err = inc_err(got, z + cfg.dt * v, z)
     print(f"identity-block step: {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- diffusion cache
+def _cache_run(cfg, model, steps, z0, cond, cc, cn, g=5.0):
+    """Run (mode, tau) steps through wan_denoise_step_cached; returns the final latent."""
+    lib, t = W(), torch()
+    cache = lib.diffusion_cache(cfg, cfg.n_blocks)
+    ws = lib.workspace(cfg, native().ENTRY_STEP)
+    zd = to_dev(z0)
+    cd = to_dev(cond) if cond is not None else None
+    ccd, cnd = ctx_dev(cfg, cc), ctx_dev(cfg, cn)
+    for mode, tau in steps:
+        if mode == 0:
+            lib.denoise_step(cfg, model, zd, cd, ccd, cnd, tau, 0.05, g, ws)
+        else:
+            lib.denoise_step_cached(cfg, model, zd, cd, ccd, cnd, tau, 0.05, g, mode, cache, ws)
+    t.cuda.synchronize()
+    return zd.cpu().numpy()
+
+
+def _cache_case(name):
+    cfg = S.get_config(name)
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    return cfg, mw, bw, S.latent(cfg), S.condition(cfg), S.context(cfg, "cond"), S.context(cfg, "null")
+
+
+@pytest.mark.parametrize("name", ["toy_step", "mid_step_bf16"])
+def test_cache_store_and_same_state_reuse_match_the_plain_step(name):
+    cfg, mw, bw, z, cond, cc, cn = _cache_case(name)
+    announce(f"cache same-state {name}")
+    model = device_model(cfg, mw, bw)
+    plain = _cache_run(cfg, model, [(0, 500.0)], z, cond, cc, cn)
+    stored = _cache_run(cfg, model, [(native().CACHE_STORE, 500.0)], z, cond, cc, cn)
+    np.testing.assert_array_equal(stored, plain)
+    # reusing what was stored at the very same state reproduces the step
+    for mode in (native().CACHE_REUSE_ATTN, native().CACHE_REUSE_UNCOND,
+                 native().CACHE_REUSE_ATTN | native().CACHE_REUSE_UNCOND):
+        lib, t = W(), torch()
+        cache = lib.diffusion_cache(cfg, cfg.n_blocks)
+        ws = lib.workspace(cfg, native().ENTRY_STEP)
+        ccd, cnd = ctx_dev(cfg, cc), ctx_dev(cfg, cn)
+        cd = to_dev(cond) if cond is not None else None
+        z1 = to_dev(z)
+        lib.denoise_step_cached(cfg, model, z1, cd, ccd, cnd, 500.0, 0.05, 5.0, native().CACHE_STORE, cache, ws)
+        z2 = to_dev(z)
+        lib.denoise_step_cached(cfg, model, z2, cd, ccd, cnd, 500.0, 0.05, 5.0, mode, cache, ws)
+        t.cuda.synchronize()
+        err = rel_err(z2.cpu().numpy() - z, plain - z)
+        print(f"{name} mode {mode} same state: {err:.3e}")
+        assert err <= 1e-6
+
+
+@pytest.mark.parametrize("name", ["toy_step", "mid_step_bf16"])
+@pytest.mark.parametrize("mode", [2, 4, 6])
+def test_cache_store_then_reuse_matches_oracle(name, mode):
+    """A store step then a reuse step at a later time, against the oracle's own cache."""
+    cfg, mw, bw, z, cond, cc, cn = _cache_case(name)
+    announce(f"cache store+reuse {name} mode {mode}")
+    model = device_model(cfg, mw, bw)
+    got = _cache_run(cfg, model, [(native().CACHE_STORE, 500.0), (mode, 450.0)], z, cond, cc, cn)
+    cache = {}
+    z1 = O.denoise_step_cached(z, cond, cc, cn, mw, bw, cfg.heads, 500.0, 0.05, 5.0, O.CACHE_STORE, cache,
+                               cfg.img_len)
+    z2 = O.denoise_step_cached(z1, cond, cc, cn, mw, bw, cfg.heads, 450.0, 0.05, 5.0, mode, cache, cfg.img_len)
+    err = inc_err(got, z2, z)
+    print(f"{name} store+reuse mode {mode}: rel err of the two-step increment {err:.3e}")
+    assert err <= TOL[cfg.mode]

@@ -14,6 +14,7 @@ from ._native import WanError  # noqa: F401
 from .synth import WanConfig
 
 __all__ = ["shape_of", "DeviceBlock", "DeviceModel", "workspace", "workspace_bytes", "patchify", "time_embed",
+           "cache_bytes", "diffusion_cache", "denoise_step_cached",
            "dit_block_forward", "head", "denoise_step", "timing_enable", "timing_read", "WanError"]
 
 
@@ -137,6 +138,33 @@ def timing_read(kernel_class: int, reset: bool = True):
     n = ctypes.c_longlong(0)
     N.check(N.load().wan_timing_read(kernel_class, ctypes.byref(ms), ctypes.byref(n), 1 if reset else 0))
     return ms.value, n.value
+
+
+def cache_bytes(cfg: WanConfig, n_blocks: int) -> int:
+    """wan_cache_bytes: device bytes of the diffusion cache for cfg's shape and n_blocks blocks."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    st = ctypes.c_int(0)
+    n = lib.wan_cache_bytes(ctypes.byref(sh), int(n_blocks), ctypes.byref(st))
+    N.check(st.value)
+    return int(n)
+
+
+def diffusion_cache(cfg: WanConfig, n_blocks: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(cache_bytes(cfg, n_blocks), dtype=torch.uint8, device=device)
+
+
+def denoise_step_cached(cfg, model: DeviceModel, z, cond, ctx_cond, ctx_null, timestep, dt, guide_scale, mode,
+                        cache, ws, stream=None):
+    """wan_denoise_step_cached: one CFG + Euler step under a diffusion-cache mode (CACHE_*)."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    N.check(lib.wan_denoise_step_cached(ctypes.byref(sh), ctypes.byref(model.struct), _ptr(z), _ptr(cond),
+                                        _ptr(ctx_cond), _ptr(ctx_null), float(timestep), float(dt),
+                                        float(guide_scale), int(mode), _ptr(cache), cache.numel(), _ptr(ws),
+                                        ws.numel(), _stream(stream)))
+    return z
 
 
 def denoise_step(cfg, model: DeviceModel, z, cond, ctx_cond, ctx_null, timestep, dt, guide_scale, ws, stream=None):

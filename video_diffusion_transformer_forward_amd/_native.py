@@ -26,7 +26,12 @@ ENTRY_TIME_EMBED = 3
 ENTRY_HEAD = 4
 
 EXPORTS = ("wan_status_str", "wan_workspace_bytes", "wan_patchify", "wan_time_embed",
-           "wan_dit_block_forward", "wan_head", "wan_denoise_step", "wan_timing_enable", "wan_timing_read")
+           "wan_dit_block_forward", "wan_head", "wan_denoise_step", "wan_cache_bytes",
+           "wan_denoise_step_cached", "wan_timing_enable", "wan_timing_read")
+
+CACHE_STORE = 1
+CACHE_REUSE_ATTN = 2
+CACHE_REUSE_UNCOND = 4
 
 KERNEL_SELF_ATTENTION = 0
 KERNEL_CROSS_ATTENTION = 1
@@ -92,6 +97,12 @@ def load(path: str = LIB_PATH):
     lib.wan_denoise_step.restype = ctypes.c_int
     lib.wan_denoise_step.argtypes = [sp, ctypes.POINTER(WanModelWeights), _vp, _vp, _vp, _vp, ctypes.c_float,
                                      ctypes.c_float, ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+    lib.wan_cache_bytes.restype = ctypes.c_size_t
+    lib.wan_cache_bytes.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.wan_denoise_step_cached.restype = ctypes.c_int
+    lib.wan_denoise_step_cached.argtypes = [sp, ctypes.POINTER(WanModelWeights), _vp, _vp, _vp, _vp, ctypes.c_float,
+                                            ctypes.c_float, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp,
+                                            ctypes.c_size_t, _vp]
     lib.wan_timing_enable.restype = ctypes.c_int
     lib.wan_timing_enable.argtypes = [ctypes.c_int]
     lib.wan_timing_read.restype = ctypes.c_int

@@ -18,6 +18,7 @@ constexpr size_t ALIGN = 256;
 constexpr int MAX_DIM = 5120;  // the LayerNorm kernel keeps one row in a wave's registers
 constexpr int MAX_CTX = 65536;
 constexpr int MAX_TOKENS = 1 << 20;
+constexpr int MAX_BLOCKS = 1024;
 constexpr int TIME_DIM = 256;
 
 size_t al(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -167,7 +168,7 @@ int check_model_weights(const wan_model_weights* w, const Dims& d, bool blocks) 
   int rc = check_ptrs({w->pe_w, w->pe_b, w->t1_w, w->t1_b, w->t2_w, w->t2_b, w->m_w, w->m_b, w->hd_w, w->hd_b});
   if (rc) return rc;
   if (blocks) {
-    if (w->n_blocks < 0 || w->n_blocks > 1024) return WAN_E_SHAPE;
+    if (w->n_blocks < 0 || w->n_blocks > MAX_BLOCKS) return WAN_E_SHAPE;
     if (w->n_blocks > 0 && !w->blocks) return WAN_E_NULL;
     for (int i = 0; i < w->n_blocks; ++i) {
       rc = check_block_weights(&w->blocks[i], d);
@@ -256,9 +257,13 @@ hipError_t timed(int cls, hipStream_t st, F&& launch) {
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// Self-attention output handling of one block run (diffusion cache)
+enum AttnMode { ATTN_COMPUTE = 0, ATTN_STORE = 1, ATTN_REUSE = 2 };
+
 template <typename T>
 int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const float* mod, long long mbs,
-              const void* ctx, void* ws, const BlockPlan& p, bool rope_ready, hipStream_t st) {
+              const void* ctx, void* ws, const BlockPlan& p, bool rope_ready, hipStream_t st,
+              int attn_mode = ATTN_COMPUTE, void* attn_io = nullptr) {
   const int M = Bb * d.L;
   T* m = reinterpret_cast<T*>(at(ws, p.m));
   T* o = reinterpret_cast<T*>(at(ws, p.o));
@@ -272,7 +277,10 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     HIP_TRY(launch_rope_tokens(ropet, rope, d.hd, d.F, d.Hh, d.Ww, st));
   }
 
-  // self-attention sublayer
+  // self-attention sublayer (its attention output optionally written to, or
+  // taken from, the diffusion cache)
+  T* a_out = attn_mode == ATTN_COMPUTE ? o : reinterpret_cast<T*>(attn_io);
+  if (attn_mode != ATTN_REUSE) {
   HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, mod + 0 * d.D, mod + 1 * d.D, mbs, st); }));
   HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.vt), Bb * d.heads, d.hd, d.L, d.Lp, st));
   {
@@ -290,13 +298,14 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     AttnArgs a;
     a.q = at(ws, p.q); a.Lq = d.L; a.Lqp = d.Lp;
     a.k[0] = at(ws, p.k); a.vt[0] = at(ws, p.vt); a.Lk[0] = d.L; a.Lkp[0] = d.Lp; a.nsrc = 1; a.self = 1;
-    a.o = o; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
+    a.o = a_out; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
     HIP_TRY(timed(WAN_KERNEL_SELF_ATTENTION, st, [&] { return launch_attention<T>(a, st); }));
+  }
   }
   {
     GemmArgs g;
     g.M = M; g.N = d.D; g.K = d.D;
-    g.A = o; g.lda = d.D; g.a_rpb = M;
+    g.A = a_out; g.lda = d.D; g.a_rpb = M;
     g.Wt = w->o_w; g.ldw = d.D; g.bias = w->o_b;
     g.c_rpb = d.L; g.x = x; g.ldx = d.D; g.gate = mod + 2 * d.D; g.gate_bstride = mbs;
     HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_RESID, st); }));
@@ -415,6 +424,70 @@ int run_head(const Dims& d, int Bb, const wan_model_weights* w, const float* x, 
 
 using namespace wan;
 
+// Diffusion cache layout: n_blocks self-attention outputs (2B, L, D), then the
+// unconditional head output (B, L, out_ch*4) float32.
+size_t cache_attn_slot(const Dims& d) { return al((size_t)2 * d.B * d.L * d.D * d.es); }
+size_t cache_bytes(const Dims& d, int n_blocks) {
+  return (size_t)n_blocks * cache_attn_slot(d) + al((size_t)d.B * d.L * 64 * 4);
+}
+
+// One CFG Euler step; mode 0 = plain, else a WAN_CACHE_* mode with `cache`.
+template <typename T>
+int run_step(const Dims& d, const wan_model_weights* w, float* z, const float* cnd, const void* ctx_cond,
+             const void* ctx_null, float timestep, float dt, float guide_scale, int mode, char* cache,
+             void* ws, const StepPlan& p, hipStream_t st) {
+  const bool uncond_cached = (mode & WAN_CACHE_REUSE_UNCOND) != 0;
+  const int nb = uncond_cached ? d.B : 2 * d.B;  // batch rows: cond videos, then null videos
+  float* x = reinterpret_cast<float*>(at(ws, p.x));
+  float* mod = reinterpret_cast<float*>(at(ws, p.mod));
+  float* pbuf = reinterpret_cast<float*>(at(ws, p.p));
+  void* ctx2 = at(ws, p.ctx);
+  const size_t ctx_bytes = (size_t)d.B * d.Lc * d.D * d.es;
+  HIP_TRY(copy_async(ctx2, ctx_cond, ctx_bytes, st));
+  if (!uncond_cached) HIP_TRY(copy_async(static_cast<char*>(ctx2) + ctx_bytes, ctx_null, ctx_bytes, st));
+  int rc;
+  if ((rc = run_time<T>(d, w, timestep, mod, (float*)at(ws, p.t1), (float*)at(ws, p.t2), st))) return rc;
+  if ((rc = run_patchify<T>(d, nb, z, cnd, w->pe_w, w->pe_b, x, st))) return rc;
+  const int amode = mode == WAN_CACHE_STORE ? ATTN_STORE : ((mode & WAN_CACHE_REUSE_ATTN) ? ATTN_REUSE : ATTN_COMPUTE);
+  for (int i = 0; i < w->n_blocks; ++i) {
+    void* aio = cache ? cache + (size_t)i * cache_attn_slot(d) : nullptr;
+    if ((rc = run_block<T>(d, nb, &w->blocks[i], x, mod, 0, ctx2, ws, p.blk, i > 0, st, amode, aio))) return rc;
+  }
+  if ((rc = run_head<T>(d, nb, w, x, at(ws, p.blk.m), pbuf, st))) return rc;
+  const size_t pu_rows = (size_t)d.B * d.L * 64;
+  float* cache_pu = cache ? reinterpret_cast<float*>(cache + (size_t)w->n_blocks * cache_attn_slot(d)) : nullptr;
+  if (mode == WAN_CACHE_STORE) HIP_TRY(copy_async(cache_pu, pbuf + pu_rows, pu_rows * sizeof(float), st));
+  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] {
+    return launch_unpatch(pbuf, z, d.B, 16, d.F, d.H, d.W, 1, dt, guide_scale, st, uncond_cached ? cache_pu : nullptr);
+  }));
+  return WAN_OK;
+}
+
+int step_entry(const wan_shape* s, const wan_model_weights* w, float* z, const float* cond, const void* ctx_cond,
+               const void* ctx_null, float timestep, float dt, float guide_scale, int mode, void* cache,
+               size_t cache_size, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if ((rc = check_model_weights(w, d, true))) return rc;
+  if ((rc = check_ptrs({z, ctx_cond, ctx_null}))) return rc;
+  if (d.Cin == 36 && (rc = check_ptrs({cond}))) return rc;
+  if (!isfinite(timestep) || !isfinite(dt) || !isfinite(guide_scale)) return WAN_E_SHAPE;
+  if (mode) {
+    if ((rc = check_ptrs({cache}))) return rc;
+    if (cache_size < cache_bytes(d, w->n_blocks)) return WAN_E_WORKSPACE;
+  }
+  const StepPlan p = plan_step(d);
+  if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float* cnd = d.Cin == 36 ? cond : nullptr;
+  char* c = static_cast<char*>(cache);
+  return d.mode == WAN_BF16
+             ? run_step<bf16>(d, w, z, cnd, ctx_cond, ctx_null, timestep, dt, guide_scale, mode, c, ws, p, st)
+             : run_step<float>(d, w, z, cnd, ctx_cond, ctx_null, timestep, dt, guide_scale, mode, c, ws, p, st);
+}
+
 extern "C" {
 
 const char* wan_status_str(int code) {
@@ -518,41 +591,28 @@ int wan_head(const wan_shape* s, const wan_model_weights* w, const float* x, flo
 int wan_denoise_step(const wan_shape* s, const wan_model_weights* w, float* z, const float* cond,
                      const void* ctx_cond, const void* ctx_null, float timestep, float dt, float guide_scale,
                      void* ws, size_t ws_bytes, void* stream) {
+  return step_entry(s, w, z, cond, ctx_cond, ctx_null, timestep, dt, guide_scale, 0, nullptr, 0, ws, ws_bytes,
+                    stream);
+}
+
+size_t wan_cache_bytes(const wan_shape* s, int n_blocks, int* status) {
   Dims d;
   int rc = check_shape(s, &d);
-  if (rc) return rc;
-  if ((rc = check_model_weights(w, d, true))) return rc;
-  if ((rc = check_ptrs({z, ctx_cond, ctx_null}))) return rc;
-  if (d.Cin == 36 && (rc = check_ptrs({cond}))) return rc;
-  if (!isfinite(timestep) || !isfinite(dt) || !isfinite(guide_scale)) return WAN_E_SHAPE;
-  const StepPlan p = plan_step(d);
-  if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
-  if ((rc = check_device())) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int B2 = 2 * d.B;
-  float* x = reinterpret_cast<float*>(at(ws, p.x));
-  float* mod = reinterpret_cast<float*>(at(ws, p.mod));
-  float* pbuf = reinterpret_cast<float*>(at(ws, p.p));
-  void* ctx2 = at(ws, p.ctx);
-  const size_t ctx_bytes = (size_t)d.B * d.Lc * d.D * d.es;
-  HIP_TRY(copy_async(ctx2, ctx_cond, ctx_bytes, st));
-  HIP_TRY(copy_async(static_cast<char*>(ctx2) + ctx_bytes, ctx_null, ctx_bytes, st));
-  const float* cnd = d.Cin == 36 ? cond : nullptr;
-  if (d.mode == WAN_BF16) {
-    if ((rc = run_time<bf16>(d, w, timestep, mod, (float*)at(ws, p.t1), (float*)at(ws, p.t2), st))) return rc;
-    if ((rc = run_patchify<bf16>(d, B2, z, cnd, w->pe_w, w->pe_b, x, st))) return rc;
-    for (int i = 0; i < w->n_blocks; ++i)
-      if ((rc = run_block<bf16>(d, B2, &w->blocks[i], x, mod, 0, ctx2, ws, p.blk, i > 0, st))) return rc;
-    if ((rc = run_head<bf16>(d, B2, w, x, at(ws, p.blk.m), pbuf, st))) return rc;
-  } else {
-    if ((rc = run_time<float>(d, w, timestep, mod, (float*)at(ws, p.t1), (float*)at(ws, p.t2), st))) return rc;
-    if ((rc = run_patchify<float>(d, B2, z, cnd, w->pe_w, w->pe_b, x, st))) return rc;
-    for (int i = 0; i < w->n_blocks; ++i)
-      if ((rc = run_block<float>(d, B2, &w->blocks[i], x, mod, 0, ctx2, ws, p.blk, i > 0, st))) return rc;
-    if ((rc = run_head<float>(d, B2, w, x, at(ws, p.blk.m), pbuf, st))) return rc;
-  }
-  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_unpatch(pbuf, z, d.B, 16, d.F, d.H, d.W, 1, dt, guide_scale, st); }));
-  return WAN_OK;
+  if (rc == WAN_OK && (n_blocks < 1 || n_blocks > MAX_BLOCKS)) rc = WAN_E_SHAPE;
+  if (status) *status = rc;
+  return rc == WAN_OK ? cache_bytes(d, n_blocks) : 0;
+}
+
+int wan_denoise_step_cached(const wan_shape* s, const wan_model_weights* w, float* z, const float* cond,
+                            const void* ctx_cond, const void* ctx_null, float timestep, float dt, float guide_scale,
+                            int cache_mode, void* cache, size_t cache_bytes_, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (cache_mode != WAN_CACHE_STORE && cache_mode != WAN_CACHE_REUSE_ATTN && cache_mode != WAN_CACHE_REUSE_UNCOND &&
+      cache_mode != (WAN_CACHE_REUSE_ATTN | WAN_CACHE_REUSE_UNCOND))
+    return WAN_E_MODE;
+  if (!cache) return WAN_E_NULL;
+  return step_entry(s, w, z, cond, ctx_cond, ctx_null, timestep, dt, guide_scale, cache_mode, cache, cache_bytes_,
+                    ws, ws_bytes, stream);
 }
 
 int wan_timing_enable(int on) {

@@ -247,9 +247,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ Wt, con
 }
 
 // out[b][c][f][y][x] from the head rows p[(b, token)][c*4 + (y%2)*2 + x%2].
-// step: out holds z; z += dt * (p_null + g (p_cond - p_null)), p_null = rows of batch B + b.
-__global__ void unpatch_kernel(const float* __restrict__ p, float* __restrict__ out, int B, int C, int F, int H,
-                               int W, int step, float dt, float guide) {
+// step: out holds z; z += dt * (p_null + g (p_cond - p_null)), p_null rows (b, token) of `pn`.
+__global__ void unpatch_kernel(const float* __restrict__ p, const float* __restrict__ pn, float* __restrict__ out,
+                               int B, int C, int F, int H, int W, int step, float dt, float guide) {
   const long long n = (long long)B * C * F * H * W;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
@@ -268,7 +268,7 @@ __global__ void unpatch_kernel(const float* __restrict__ p, float* __restrict__ 
   if (!step) {
     out[idx] = pc;
   } else {
-    const float pu = p[((long long)(B + b) * L + tok) * K + k];
+    const float pu = pn[((long long)b * L + tok) * K + k];
     const float v = pu + guide * (pc - pu);
     out[idx] = out[idx] + dt * v;
   }
@@ -329,11 +329,13 @@ hipError_t launch_gemv(const void* Wt, const float* bias, const float* x, float 
 }
 
 hipError_t launch_unpatch(const float* p, float* out, int B, int C, int F, int H, int W, int step, float dt,
-                          float guide, hipStream_t st) {
+                          float guide, hipStream_t st, const float* p_null) {
   const long long n = (long long)B * C * F * H * W;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(unpatch_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, out, B, C, F, H, W,
-                     step, dt, guide);
+  const long long L = (long long)F * (H / 2) * (W / 2);
+  if (!p_null) p_null = p + (long long)B * L * C * 4;
+  hipLaunchKernelGGL(unpatch_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, p_null, out, B, C, F,
+                     H, W, step, dt, guide);
   return hipGetLastError();
 }
 

@@ -88,10 +88,10 @@ hipError_t launch_gemv(const void* Wt, const float* bias, const float* x, float 
                        int silu_in, hipStream_t st);
 
 // Unpatchify the head output p (rows of out_ch*4) and either store it (dt == 0 && !step)
-// or apply guidance + Euler to z.  Branch layout: p rows [0, B*L) conditional,
-// [B*L, 2*B*L) null when `step`.
+// or apply guidance + Euler to z.  With `step`, p rows [0, B*L) are the conditional
+// branch and p_null (default: p rows [B*L, 2*B*L)) the unconditional one.
 hipError_t launch_unpatch(const float* p, float* out, int B, int C, int F, int H, int W, int step, float dt,
-                          float guide, hipStream_t st);
+                          float guide, hipStream_t st, const float* p_null = nullptr);
 
 // copy helper (device to device, on the stream)
 hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t st);
