@@ -69,6 +69,31 @@ def step_flops(cfg: S.WanConfig) -> float:
     return cfg.n_blocks * per_block + patch + head + time_mlp
 
 
+def time_block(bcfg: S.WanConfig, reps: int = 5) -> dict:
+    """ms and TFLOP/s of one wan_dit_block_forward on a single video of bcfg's shape (inputs resident)."""
+    import torch
+    import video_diffusion_transformer_forward_amd as W
+    from video_diffusion_transformer_forward_amd import _native as N
+    blk = W.DeviceBlock(bcfg, S.block_weights(bcfg, 0))
+    x = torch.from_numpy(S.block_inputs(bcfg)).cuda()
+    mod = torch.from_numpy(S.modulation(bcfg)).cuda()
+    ctx = torch.from_numpy(S.context(bcfg, "cond")).to(W.elem_dtype(bcfg)).cuda()
+    ws = W.workspace(bcfg, N.ENTRY_BLOCK)
+    for _ in range(2):
+        W.dit_block_forward(bcfg, blk, x, mod, ctx, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        W.dit_block_forward(bcfg, blk, x, mod, ctx, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    fl = sum(block_flops(bcfg, bcfg.batch).values())
+    del blk, x, mod, ctx, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_block": round(ms, 3), "block_tflop": round(fl / 1e12, 3),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "seq_len": bcfg.seq_len, "dim": bcfg.dim}
+
+
 def attn_traffic_bytes():
     """Counted bytes per self-attention launch, or None once its sources differ from the measured ones."""
     import hashlib
@@ -92,7 +117,7 @@ def cpu_baseline(cfg: S.WanConfig, budget_s: float = 20.0) -> dict:
     mod = S.modulation(bcfg)
     ctx = S.context(bcfg, "cond")
     L, D, F = bcfg.seq_len, bcfg.dim, bcfg.ffn_dim
-    n_rows = 4096
+    n_rows = 8192
     rows = np.linspace(0, L - 1, n_rows).astype(int).tolist()
     t0 = time.perf_counter()
     O.dit_block(x, mod, ctx, w, bcfg.heads, bcfg.grid, bcfg.img_len, rows=rows)
@@ -125,6 +150,9 @@ def main():
     ap.add_argument("--config", default="wan13b_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-modes", action="store_true", help="skip timing the diffusion-cache step modes")
+    ap.add_argument("--block-configs", default="",
+                    help="comma-separated block configurations to time one block forward of "
+                         "(e.g. wan13b_block,wan14b_720p_block,wan14b_i2v_block); reported under 'blocks'")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB -> 1 GiB elementwise copy three times: the "
                          "known-size kernel that scales the HBM byte counters of a counter-collection run")
@@ -254,6 +282,11 @@ def main():
             "ms_per_step": cache_ms, "cache_gb": cache_gb,
             "note": "one CFG step per mode after a store step; a reuse step skips the QKV projection and "
                     "self-attention (reuse_attn) and/or the unconditional branch (reuse_uncond)"}
+    if args.block_configs:
+        out["blocks"] = {}
+        for name in [c for c in args.block_configs.split(",") if c]:
+            print(f"[bench] block {name}", file=sys.stderr, flush=True)
+            out["blocks"][name] = time_block(S.get_config(name))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)
