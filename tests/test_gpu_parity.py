@@ -387,3 +387,38 @@ def test_cache_store_then_reuse_matches_oracle(name, mode):
     err = inc_err(got, z2, z)
     print(f"{name} store+reuse mode {mode}: rel err of the two-step increment {err:.3e}")
     assert err <= TOL[cfg.mode]
+
+
+@pytest.mark.parametrize("name,batch", [("toy_i2v_fp32", 1), ("mid_step_bf16", 2)])
+def test_cache_i2v_and_two_videos(name, batch):
+    """The cached step with image conditioning (two-source cross-attention) and with two videos per
+    call (CFG batch 4), store then reuse of both the attention and the unconditional velocity."""
+    cfg = S.get_config(name).with_(batch=batch, n_blocks=2)
+    announce(f"cache {name} batch {batch}")
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    z, cond = S.latent(cfg), S.condition(cfg)
+    cc, cn = S.context(cfg, "cond"), S.context(cfg, "null")
+    model = device_model(cfg, mw, bw)
+    both = native().CACHE_REUSE_ATTN | native().CACHE_REUSE_UNCOND
+    got = _cache_run(cfg, model, [(native().CACHE_STORE, 500.0), (both, 450.0)], z, cond, cc, cn)
+    cache = {}
+    z1 = O.denoise_step_cached(z, cond, cc, cn, mw, bw, cfg.heads, 500.0, 0.05, 5.0, O.CACHE_STORE, cache,
+                               cfg.img_len)
+    z2 = O.denoise_step_cached(z1, cond, cc, cn, mw, bw, cfg.heads, 450.0, 0.05, 5.0, both, cache, cfg.img_len)
+    err = inc_err(got, z2, z)
+    print(f"{name} batch {batch} store+reuse: {err:.3e}")
+    assert err <= TOL[cfg.mode]
+
+
+def test_step_two_videos():
+    """One plain step over two videos at once (CFG batch 4) against the oracle."""
+    cfg = S.get_config("mid_step_bf16").with_(batch=2, n_blocks=2)
+    announce("step two videos")
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    z = S.latent(cfg)
+    cc, cn = S.context(cfg, "cond"), S.context(cfg, "null")
+    got = gpu_step(cfg, mw, bw, z, None, cc, cn, 300.0, 0.05, 5.0)
+    ref = O.denoise_step(z, None, cc, cn, mw, bw, cfg.heads, 300.0, 0.05, 5.0)
+    assert inc_err(got, ref, z) <= TOL["bf16"]
