@@ -208,8 +208,45 @@ def attention(q, k, v, chunk=4096):
     return out
 
 
-def multihead_attention(q, k, v, heads):
-    """q: (B, Lq, D), k/v: (B, Lk, D); head h uses features [h*d, (h+1)*d)."""
+# --------------------------------------------------------------------------- 8-bit Q K^T
+E4M3_MAX = 448.0
+
+
+def e4m3_round(x):
+    """Nearest float8 e4m3 value (4 exponent bits with bias 7, 3 mantissa bits,
+    subnormal spacing 2^-9, largest finite value 448), ties to the even code.
+    Inputs must satisfy |x| <= 448."""
+    x = f64(x)
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, -6.0)           # below 2^-6 the spacing stays 2^-9 (subnormals)
+    step = np.exp2(e - 3.0)
+    return np.sign(x) * np.round(ax / step) * step   # np.round: half to even
+
+
+def quantize_rows_e4m3(x):
+    """8-bit form of q or k ([P2] method: FP8 GEMM and 8-bit FlashAttention at
+    inference; the scaling rule is this build's reading): every row (one token of
+    one head) is rounded to float32, given the power-of-two scale 2^e with the
+    smallest e such that max|row| / 2^e <= 448, and rounded to e4m3 in that scale.
+    Returns the dequantized rows (float64) and the exponents e."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    amax = np.abs(x32).max(axis=-1)
+    mant, ex = np.frexp(amax)           # amax = mant * 2^ex, mant in [0.5, 1)
+    e = np.where(amax > 0, ex - 9 + (mant > 0.875), 0).astype(np.int64)
+    scale = np.exp2(e.astype(np.float64))[..., None]
+    return e4m3_round(x32 / scale) * scale, e
+
+
+def attention_qk8(q, k, v, chunk=4096):
+    """attention() with q and k in their 8-bit form (quantize_rows_e4m3, per token);
+    the probabilities and v stay exact."""
+    return attention(quantize_rows_e4m3(q)[0], quantize_rows_e4m3(k)[0], v, chunk)
+
+
+def multihead_attention(q, k, v, heads, qk8=False):
+    """q: (B, Lq, D), k/v: (B, Lk, D); head h uses features [h*d, (h+1)*d).
+    qk8: q and k of every head in their 8-bit form (attention_qk8)."""
     q, k, v = f64(q), f64(k), f64(v)
     B, Lq, D = q.shape
     d = D // heads
@@ -217,7 +254,8 @@ def multihead_attention(q, k, v, heads):
     for b in range(B):
         for h in range(heads):
             sl = slice(h * d, (h + 1) * d)
-            out[b, :, sl] = attention(q[b, :, sl], k[b, :, sl], v[b, :, sl])
+            att = attention_qk8 if qk8 else attention
+            out[b, :, sl] = att(q[b, :, sl], k[b, :, sl], v[b, :, sl])
     return out
 
 
@@ -226,7 +264,7 @@ def _lin(x, w, b):
     return f64(x) @ f64(w).T + f64(b)
 
 
-def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None):
+def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8=False):
     """Self-attention sublayer output (before its gate).
 
     q, k, v = m W_qkv^T + b_qkv (rows of W_qkv ordered [q; k; v]); RoPE on q and
@@ -235,7 +273,8 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None):
     rows: token indices whose outputs are wanted (None = all).
     attn: a cached attention output (B, L, D) (heads concatenated, before W_o)
     used instead of computing q, k, v and the attention (the diffusion cache);
-    record: a list that receives the attention output computed here.
+    record: a list that receives the attention output computed here;
+    qk8: the scores from q and k in their 8-bit form (attention_qk8).
     """
     if attn is not None:
         a = f64(attn) if rows is None else f64(attn)[:, rows]
@@ -249,7 +288,7 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None):
     mq = m_all if rows is None else m_all[:, rows]
     n = mq.shape[1]
     q = rope_apply(_lin(mq, wq, bq).reshape(B, n, heads, d), grid, rows).reshape(B, n, D)
-    a = multihead_attention(q, k, v, heads)
+    a = multihead_attention(q, k, v, heads, qk8)
     if record is not None:
         record.append(a)
     return _lin(a, w["o_w"], w["o_b"])
@@ -282,7 +321,7 @@ def ffn(xm, w):
     return _lin(gelu(_lin(xm, w["ff1_w"], w["ff1_b"])), w["ff2_w"], w["ff2_b"])
 
 
-def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, record=None):
+def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, record=None, qk8=False):
     """One DiT block, residual stream in float64.
 
         x <- x + g1 * SA(LN(x) (1 + sc1) + sh1)
@@ -293,7 +332,7 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
     scale2, gate2); ctx: (B, L_img + L_txt, D).
     rows: if given, return only those tokens' outputs (the keys and values of
     self-attention still come from every token) -> (B, len(rows), D).
-    attn / record: see self_attention (diffusion cache).
+    attn / record: see self_attention (diffusion cache); qk8: 8-bit q k^T in self-attention.
     """
     x = f64(x)
     mod = f64(mod)
@@ -302,7 +341,7 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
     sh1, sc1, g1, sh2, sc2, g2 = [mod[:, i][:, None, :] for i in range(6)]
     m_all = modulate(layer_norm(x), sh1, sc1)
     xr = x if rows is None else x[:, rows]
-    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record)
+    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record, qk8)
     xr = xr + cross_attention(layer_norm(xr), ctx, w, heads, img_len)
     xr = xr + g2 * ffn(modulate(layer_norm(xr), sh2, sc2), w)
     return xr
@@ -330,7 +369,7 @@ def euler_update(z, v, dt):
     return f64(z) + dt * f64(v)
 
 
-def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0, attn_cache=None, record=None):
+def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0, attn_cache=None, record=None, qk8=False):
     """Velocity prediction of the whole DiT for one context: (B, 16, F, H, W).
 
     attn_cache: per-block cached self-attention outputs to use instead of
@@ -343,16 +382,16 @@ def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0, attn_cac
                           model_w["t2_b"], model_w["m_w"], model_w["m_b"])
     for i, w in enumerate(blocks_w):
         x = dit_block(x, mod, ctx, w, heads, grid, img_len,
-                      attn=None if attn_cache is None else attn_cache[i], record=record)
+                      attn=None if attn_cache is None else attn_cache[i], record=record, qk8=qk8)
     p = head(x, model_w["hd_w"], model_w["hd_b"])
     return patch_scatter(p, F, H, W)
 
 
 def denoise_step(z, cond, ctx_cond, ctx_null, model_w, blocks_w, heads, tau, dt,
-                 guide_scale, img_len=0):
+                 guide_scale, img_len=0, qk8=False):
     """One CFG denoise step: both branches, guidance combine, Euler update."""
-    v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len)
-    v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len)
+    v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len, qk8=qk8)
+    v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len, qk8=qk8)
     return euler_update(z, cfg_combine(v_c, v_u, guide_scale), dt)
 
 

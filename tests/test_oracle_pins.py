@@ -528,3 +528,65 @@ def test_cache_reuse_uncond_guidance_limits():
     np.testing.assert_allclose(c, z2 + 0.05 * cache["v_u"], rtol=1e-12, atol=1e-13)
     with pytest.raises(ValueError):
         O.denoise_step_cached(z2, None, ctx_c, ctx_n, mw, blocks, H, 350.0, 0.05, 1.0, 8, cache)
+
+
+# ----------------------------------------------------------------------------- 8-bit q k^T
+def _e4m3_grid():
+    """Every finite non-negative e4m3 value from its bit fields (bias 7, 3 mantissa bits)."""
+    vals = []
+    for code in range(0x7F):             # 0x7F is NaN
+        ex, man = code >> 3, code & 7
+        vals.append((man / 8.0) * 2.0 ** -6 if ex == 0 else (1 + man / 8.0) * 2.0 ** (ex - 7))
+    return np.array(vals)
+
+
+def test_e4m3_round_is_nearest_with_ties_to_even():
+    grid = _e4m3_grid()
+    assert grid.max() == 448.0 and grid[1] == 2.0 ** -9
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-0.05, 0.05, 2000),
+                        (grid[:-1] + grid[1:]) / 2])          # exact midpoints: ties
+    r = O.e4m3_round(x)
+    for xi, ri in zip(x, r):
+        ax = abs(xi)
+        d = np.abs(grid - ax)
+        best = np.flatnonzero(d == d.min())
+        code = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]   # even mantissa code
+        assert abs(ri) == grid[code] and (ri == 0 or np.sign(ri) == np.sign(xi)), (xi, ri)
+
+
+def test_row_scale_exponent_is_the_smallest_fitting_power_of_two():
+    x = rng.standard_normal((300, 16)) * np.exp2(rng.integers(-20, 20, (300, 1)))
+    x[0] = 0.0
+    x[1:3] = 1.0
+    x[1, 3] = 448.0
+    x[2, 0] = 449.0
+    _, e = O.quantize_rows_e4m3(x)
+    amax = np.abs(x.astype(np.float32).astype(np.float64)).max(axis=1)
+    for a, ei in zip(amax, e):
+        if a == 0:
+            assert ei == 0
+            continue
+        assert a / 2.0 ** ei <= 448.0 and a / 2.0 ** (ei - 1) > 448.0
+    assert e[1] == 0 and e[2] == 1
+
+
+def test_qk8_attention_exact_on_representable_inputs_and_bounded_otherwise():
+    grid = _e4m3_grid()
+    pick = lambda shape: rng.choice(np.concatenate([grid, -grid]), shape)
+    d = 16
+    q = pick((6, d)) * 2.0 ** -7
+    k = pick((9, d)) * 2.0 ** -7
+    q[:, 0] = 448.0 * 2.0 ** -7                          # every row reaches its scale's top
+    k[:, 0] = -448.0 * 2.0 ** -7
+    v = rng.standard_normal((9, d))
+    np.testing.assert_allclose(O.attention_qk8(q, k, v), O.attention(q, k, v), rtol=1e-13, atol=1e-14)
+    # random rows: each element moves by at most half an e4m3 step in its row's scale
+    q = rng.standard_normal((40, 64))
+    qq, e = O.quantize_rows_e4m3(q)
+    step_bound = np.exp2(e[:, None] + np.maximum(np.floor(np.log2(np.abs(q) / np.exp2(e[:, None]) + 1e-300)), -6) - 4)
+    assert np.all(np.abs(qq - q) <= step_bound * (1 + 1e-9) + 1e-12)
+    k = rng.standard_normal((50, 64))
+    v = rng.standard_normal((50, 64))
+    ref = O.attention(q, k, v)
+    err = np.linalg.norm(O.attention_qk8(q, k, v) - ref) / np.linalg.norm(ref)
+    assert 1e-4 < err < 5e-2
