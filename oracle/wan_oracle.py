@@ -238,6 +238,14 @@ def quantize_rows_e4m3(x):
     return e4m3_round(x32 / scale) * scale, e
 
 
+def round_bf16_rne(a):
+    """Nearest bfloat16 value of float32(a), ties to even (bfloat16 is the upper
+    half of a float32: 8 exponent bits, 7 mantissa bits)."""
+    u = np.asarray(a, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def attention_qk8(q, k, v, chunk=4096):
     """attention() with q and k in their 8-bit form (quantize_rows_e4m3, per token);
     the probabilities and v stay exact."""
@@ -274,7 +282,10 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8
     attn: a cached attention output (B, L, D) (heads concatenated, before W_o)
     used instead of computing q, k, v and the attention (the diffusion cache);
     record: a list that receives the attention output computed here;
-    qk8: the scores from q and k in their 8-bit form (attention_qk8).
+    qk8: the scores from q and k in their 8-bit form (attention_qk8).  The 8-bit
+    rounding is a decision taken on q and k, so it is taken on the values the
+    library decides on: q and k projected from the bfloat16 form of m (the
+    operand precision of the projection in bf16 mode), see round_bf16_rne.
     """
     if attn is not None:
         a = f64(attn) if rows is None else f64(attn)[:, rows]
@@ -283,9 +294,10 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8
     d = D // heads
     wq, wk, wv = np.split(f64(w["qkv_w"]), 3, axis=0)
     bq, bk, bv = np.split(f64(w["qkv_b"]), 3)
-    k = rope_apply(_lin(m_all, wk, bk).reshape(B, L, heads, d), grid).reshape(B, L, D)
+    m_qk = round_bf16_rne(m_all) if qk8 else m_all
+    k = rope_apply(_lin(m_qk, wk, bk).reshape(B, L, heads, d), grid).reshape(B, L, D)
     v = _lin(m_all, wv, bv)
-    mq = m_all if rows is None else m_all[:, rows]
+    mq = m_qk if rows is None else m_qk[:, rows]
     n = mq.shape[1]
     q = rope_apply(_lin(mq, wq, bq).reshape(B, n, heads, d), grid, rows).reshape(B, n, D)
     a = multihead_attention(q, k, v, heads, qk8)

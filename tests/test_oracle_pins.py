@@ -590,3 +590,43 @@ def test_qk8_attention_exact_on_representable_inputs_and_bounded_otherwise():
     ref = O.attention(q, k, v)
     err = np.linalg.norm(O.attention_qk8(q, k, v) - ref) / np.linalg.norm(ref)
     assert 1e-4 < err < 5e-2
+
+
+def test_bf16_rounding_matches_torch_and_is_nearest():
+    import torch
+    x = np.concatenate([rng.standard_normal(5000) * np.exp2(rng.integers(-30, 30, 5000)),
+                        # exact float32 midpoints between neighbouring bfloat16 values: ties
+                        ((rng.integers(0x0080, 0x7F00, 2000).astype(np.uint32) << 16) | 0x8000).view(np.float32)])
+    r = O.round_bf16_rne(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(r, ref)
+    u = r.astype(np.float32).view(np.uint32)
+    assert np.all(u & 0xFFFF == 0)
+    # nearest: no bfloat16 neighbour is closer
+    x32 = x.astype(np.float32).astype(np.float64)
+    for step in (-1, 1):
+        nb = ((u.astype(np.int64) + step * 0x10000).astype(np.uint32)).view(np.float32).astype(np.float64)
+        assert np.all(np.abs(nb - x32) >= np.abs(r - x32))
+
+
+def test_qk8_self_attention_decides_on_the_bf16_activation():
+    """With a bfloat16-exact activation the 8-bit path is q k^T of the e4m3 rows, with an
+    inexact one it sees the bfloat16 activation: changing m below bfloat16 resolution
+    leaves the 8-bit scores' q and k unchanged."""
+    B, L, D, heads = 1, 12, 32, 2
+    grid = (1, 3, 4)
+    w = {"qkv_w": rng.standard_normal((3 * D, D)) * 0.3, "qkv_b": rng.standard_normal(3 * D) * 0.1,
+         "o_w": np.eye(D), "o_b": np.zeros(D)}
+    m = O.round_bf16_rne(rng.standard_normal((B, L, D)))
+    tiny = m * 2.0 ** -12 * rng.uniform(-1, 1, m.shape)        # well below half a bfloat16 step
+    a = O.self_attention(m, w, heads, grid, qk8=True)
+    b = O.self_attention(m + tiny, w, heads, grid, qk8=True)
+    # only v moved: the difference is the attention of the v change, tiny
+    assert np.max(np.abs(a - b)) < 1e-2 * np.max(np.abs(a))
+    rec_a, rec_b = [], []
+    O.self_attention(m, w, heads, grid, qk8=True, record=rec_a)
+    w_v0 = dict(w, qkv_w=w["qkv_w"].copy(), qkv_b=w["qkv_b"].copy())
+    w_v0["qkv_w"][2 * D:] = 0.0
+    w_v0["qkv_b"][2 * D:] = 1.0                                 # v = 1 everywhere: output 1 for any weights
+    O.self_attention(m + tiny, w_v0, heads, grid, qk8=True, record=rec_b)
+    np.testing.assert_allclose(rec_b[0], 1.0, rtol=1e-12)
