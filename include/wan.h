@@ -50,6 +50,17 @@ extern "C" {
 /* precision modes */
 #define WAN_BF16 0 /* bf16 GEMM/attention operands, float32 accumulation */
 #define WAN_FP32 1 /* float32 everywhere */
+/* As WAN_BF16 (same weights, context and workspace sizes), except that every
+ * self-attention takes its scores from q and k in 8-bit form ([P2] method:
+ * inference runs FP8 GEMMs and an 8-bit FlashAttention; which operands go to
+ * 8 bits and how they are scaled is this library's reading): each
+ * (token, head) row of q and of k (after RoPE) is given the power-of-two scale
+ * 2^e with the smallest e (clamped to [-127, 127]) that brings its largest
+ * magnitude to 448 or below, and is rounded to the nearest float8 e4m3 value
+ * (ties to even) in that scale; q k^T is then taken from the rounded rows.  The
+ * probabilities and v stay bf16, cross-attention is unchanged.  Needs
+ * dim / heads == 128 (WAN_E_SHAPE otherwise). */
+#define WAN_BF16_QK8 2
 
 /* entry ids for wan_workspace_bytes */
 #define WAN_ENTRY_PATCHIFY 0

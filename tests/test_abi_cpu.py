@@ -158,3 +158,22 @@ def test_no_device_reported_as_hip_error():
     except ImportError:
         pass
     assert _block_call() == N.WAN_E_HIP
+
+
+def test_qk8_mode_shapes():
+    """8-bit-score mode: same workspace as bf16 for 128-wide heads, WAN_E_SHAPE for 64-wide heads."""
+    lib = N.load()
+    st = ctypes.c_int(0)
+    for name in ("mid_bf16", "wan13b_step"):
+        cfg = get_config(name)
+        sizes = []
+        for qk8 in (False, True):
+            sh = shape_of(cfg.with_(qk8=qk8))
+            sizes.append(lib.wan_workspace_bytes(ctypes.byref(sh), N.ENTRY_STEP, ctypes.byref(st)))
+            assert st.value == N.WAN_OK
+        assert sizes[0] == sizes[1] > 0
+    sh = shape_of(get_config("toy").with_(mode="bf16", qk8=True))   # dim 256, 4 heads of 64
+    assert lib.wan_workspace_bytes(ctypes.byref(sh), N.ENTRY_BLOCK, ctypes.byref(st)) == 0
+    assert st.value == N.WAN_E_SHAPE
+    with pytest.raises(ValueError):
+        shape_of(get_config("toy").with_(qk8=True))                    # fp32 has no 8-bit form

@@ -30,7 +30,15 @@ def elem_dtype(cfg: WanConfig):
 
 def shape_of(cfg: WanConfig) -> N.WanShape:
     return N.WanShape(cfg.batch, cfg.in_ch, cfg.out_ch, cfg.frames, cfg.height, cfg.width, cfg.dim, cfg.heads,
-                      cfg.ffn_dim, cfg.txt_len, cfg.img_len, N.WAN_BF16 if cfg.mode == "bf16" else N.WAN_FP32)
+                      cfg.ffn_dim, cfg.txt_len, cfg.img_len, _mode_id(cfg))
+
+
+def _mode_id(cfg: WanConfig) -> int:
+    if cfg.mode == "bf16":
+        return N.WAN_BF16_QK8 if cfg.qk8 else N.WAN_BF16
+    if cfg.qk8:
+        raise ValueError("8-bit q k^T needs mode 'bf16'")
+    return N.WAN_FP32
 
 
 def _ptr(t):

@@ -28,18 +28,20 @@ int pad256(int x) { return (x + 255) / 256 * 256; }
 
 struct Dims {
   int B, Cin, F, H, W, Hh, Ww, L, Lp, D, heads, hd, Ff, Lt, Li, Lc, Ltp, Lip, mode;
+  bool qk8;  // self-attention scores from 8-bit q and k (WAN_BF16_QK8)
   size_t es;
 };
 
 int check_shape(const wan_shape* s, Dims* d) {
   if (!s) return WAN_E_NULL;
-  if (s->mode != WAN_BF16 && s->mode != WAN_FP32) return WAN_E_MODE;
+  if (s->mode != WAN_BF16 && s->mode != WAN_FP32 && s->mode != WAN_BF16_QK8) return WAN_E_MODE;
   if (s->batch < 1 || (s->in_ch != 16 && s->in_ch != 36) || s->out_ch != 16) return WAN_E_SHAPE;
   if (s->frames < 1 || s->height < 2 || s->width < 2 || (s->height & 1) || (s->width & 1)) return WAN_E_SHAPE;
   if (s->dim < 256 || s->dim % 256 != 0 || s->dim > MAX_DIM) return WAN_E_SHAPE;
   if (s->heads < 1 || s->dim % s->heads != 0) return WAN_E_SHAPE;
   const int hd = s->dim / s->heads;
   if (hd != 64 && hd != 128) return WAN_E_SHAPE;
+  if (s->mode == WAN_BF16_QK8 && hd != 128) return WAN_E_SHAPE;
   if (s->ffn_dim < 256 || s->ffn_dim % 256 != 0 || s->ffn_dim > (1 << 16)) return WAN_E_SHAPE;
   if (s->txt_len < 1 || s->img_len < 0 || s->txt_len + s->img_len > MAX_CTX) return WAN_E_SHAPE;
   const long long L = (long long)s->frames * (s->height / 2) * (s->width / 2);
@@ -64,8 +66,9 @@ int check_shape(const wan_shape* s, Dims* d) {
     d->Lc = s->txt_len + s->img_len;
     d->Ltp = pad64(s->txt_len);
     d->Lip = pad64(s->img_len);
-    d->mode = s->mode;
-    d->es = s->mode == WAN_BF16 ? 2 : 4;
+    d->mode = s->mode == WAN_FP32 ? WAN_FP32 : WAN_BF16;  // element type of the operands
+    d->qk8 = s->mode == WAN_BF16_QK8;
+    d->es = d->mode == WAN_BF16 ? 2 : 4;
   }
   return WAN_OK;
 }
@@ -257,6 +260,10 @@ hipError_t timed(int cls, hipStream_t st, F&& launch) {
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// bytes of e4m3 q (or k) of Bb batch rows; the scale bytes follow them inside
+// the bf16 q (k) region, which is twice as large
+size_t qk8_bytes(const Dims& d, int Bb) { return al((size_t)Bb * d.heads * d.Lp * d.hd); }
+
 // Self-attention output handling of one block run (diffusion cache)
 enum AttnMode { ATTN_COMPUTE = 0, ATTN_STORE = 1, ATTN_REUSE = 2 };
 
@@ -292,13 +299,23 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     g.q = at(ws, p.q); g.k = at(ws, p.k); g.vt = at(ws, p.vt);
     g.nq = d.D; g.nk = d.D; g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
     g.rope = ropet;
-    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
+    if (d.qk8) {
+      // e4m3 q / k take the first half of their bf16 regions, the scale bytes follow
+      g.qs = reinterpret_cast<unsigned char*>(at(ws, p.q + qk8_bytes(d, Bb)));
+      g.ks = reinterpret_cast<unsigned char*>(at(ws, p.k + qk8_bytes(d, Bb)));
+    }
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, d.qk8 ? EPI_PACK8 : EPI_PACK, st); }));
   }
   {
     AttnArgs a;
     a.q = at(ws, p.q); a.Lq = d.L; a.Lqp = d.Lp;
     a.k[0] = at(ws, p.k); a.vt[0] = at(ws, p.vt); a.Lk[0] = d.L; a.Lkp[0] = d.Lp; a.nsrc = 1; a.self = 1;
     a.o = a_out; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
+    if (d.qk8) {
+      a.qk8 = 1;
+      a.qs = reinterpret_cast<const unsigned char*>(at(ws, p.q + qk8_bytes(d, Bb)));
+      a.ks = reinterpret_cast<const unsigned char*>(at(ws, p.k + qk8_bytes(d, Bb)));
+    }
     HIP_TRY(timed(WAN_KERNEL_SELF_ATTENTION, st, [&] { return launch_attention<T>(a, st); }));
   }
   }

@@ -729,6 +729,343 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   }
 }
 
+// ---- self-attention with 8-bit scores
+//
+// q and k arrive as e4m3 bytes with one power-of-two scale per (token, head)
+// (an E8M0 byte, exponent + 127).  S^T = K Q^T runs on the scaled fp8 MFMA
+// (32x32x64), which multiplies in the key's and the query's scale itself, so
+// the scores are those of the dequantised rows up to float32 summation.  A
+// 32-key block of S over the 128-wide head is two such MFMAs (64 cycles each,
+// against eight bf16 MFMAs of 32 cycles), so a 64-key tile costs 256 matrix
+// cycles for S and 512 for the bf16 P V products.  The rest follows the bf16
+// kernel above: 8 waves of 32 queries share K / V^T rings in LDS, the
+// softmax of tile t overlaps the scores of tile t+1 and the P V products.
+// Both halves of a lane pair (l, l+32) pass the same scale byte, so the scale
+// covers the whole head whatever k-order the MFMA gives its operand bytes.
+template <int NR, int NW>
+struct Wide8Cfg {
+  static constexpr int HD = 128;
+  static constexpr int BMQ = NW * 32;                 // queries per workgroup
+  static constexpr int KT_B = ATT_BN * HD;            // bytes per fp8 K tile
+  static constexpr int VT_B = HD * ATT_BN * 2;        // bytes per bf16 V^T tile
+  static constexpr int KS_B = 256;                    // key-scale bytes per stage (64 used)
+  static constexpr int K_DMA = KT_B / (16 * 64 * NW);
+  static constexpr int V_DMA = VT_B / (16 * 64 * NW);
+  static constexpr int VRING = NR * KT_B;
+  static constexpr int SRING = VRING + NR * VT_B;
+  static constexpr size_t RING_BYTES = (size_t)SRING + NR * KS_B;
+  static constexpr size_t EPI_BYTES = (size_t)BMQ * HD * 2;
+  static constexpr size_t LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+  static_assert(K_DMA * 16 * 64 * NW == KT_B && V_DMA * 16 * 64 * NW == VT_B, "DMA split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32 operand bytes from two 16-byte LDS / global reads
+__device__ __forceinline__ i32x8 load32(const unsigned char* lo, const unsigned char* hi) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(lo);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(hi);
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// S^T(32 keys x 32 queries) += K8 Q8^T over 64 head features, scales per key row / query column
+__device__ __forceinline__ void mma8(f32x16& acc, const i32x8& k, const i32x8& q, int kscale, int qscale) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k, q, acc, 0, 0, 0, kscale, 0, qscale);
+}
+
+template <int NR, int NW>
+__device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
+  using T = bf16;
+  using Cfg = Wide8Cfg<NR, NW>;
+  constexpr int HD = Cfg::HD, BMQ = Cfg::BMQ;
+  constexpr int ND = HD / 32;              // 32-row blocks of d in O^T
+  constexpr int KBLK_B = 32 * HD;          // bytes per 32-key block of a K tile
+  constexpr int VBLK_B = 32 * 8 * 16;      // bytes per 32-row block of a V^T tile
+  static_assert(NR == 2, "ring depth");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g2 = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int nqt = (a.Lq + BMQ - 1) / BMQ;
+  const int G = nqt * a.heads * a.B;
+  const int id = xcd_remap(blockIdx.x, G);
+  const int qt = id % nqt;
+  const int bh = id / nqt;
+  const int b = bh / a.heads;
+  const int h = bh - b * a.heads;
+  const int q0 = qt * BMQ + wave * 32;
+  const float c = a.scale_log2;
+  const int Lk = a.Lk[0];
+  const int Lkp = a.Lkp[0];
+  const int n = (Lk + ATT_BN - 1) / ATT_BN;
+
+  // the wave's 32 queries: operand of MFMA s = bytes [64s + 32 g2, +32) of query l32, and its scale
+  i32x8 qf[2];
+  int qsc = 127;
+  {
+    const int qrow = q0 + l32;
+    if (qrow < a.Lq) {
+      const unsigned char* qp = reinterpret_cast<const unsigned char*>(a.q) + ((long long)bh * a.Lqp + qrow) * HD;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) qf[s] = load32(qp + 64 * s + 32 * g2, qp + 64 * s + 32 * g2 + 16);
+      qsc = a.qs[(long long)bh * a.Lqp + qrow];
+    } else {
+      const i32x8 zero = {};
+      qf[0] = zero;
+      qf[1] = zero;
+    }
+  }
+
+  // LDS offsets: K rows are 128 bytes (8 chunks, swizzled as 128-byte bf16 rows)
+  int koff[2][2], voff[4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) koff[s][hf] = (l32 * 8 + att_swz<T, 8>(l32, 4 * s + 2 * g2 + hf)) * 16;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) voff[u] = (l32 * 8 + att_swz<T, 8>(l32, 2 * u + g2)) * 16;
+
+  unsigned kdo[Cfg::K_DMA], vdo[Cfg::V_DMA];
+#pragma unroll
+  for (int i = 0; i < Cfg::K_DMA; ++i) {
+    const int P = (wave * Cfg::K_DMA + i) * 64 + lane;
+    const int r = P / 8;
+    kdo[i] = (unsigned)(r * HD + att_swz<T, 8>(r, P % 8) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::V_DMA; ++i) {
+    const int P = (wave * Cfg::V_DMA + i) * 64 + lane;
+    const int r = P / 8;
+    vdo[i] = (unsigned)(r * Lkp + att_swz<T, 8>(r, P % 8) * 8) * 2u;
+  }
+  const unsigned char* Kg = reinterpret_cast<const unsigned char*>(a.k[0]) + (long long)bh * Lkp * HD;
+  const unsigned char* Vg = reinterpret_cast<const unsigned char*>(a.vt[0]) + (long long)bh * HD * Lkp * 2;
+  // key scales: wave 0 copies a tile's 64 bytes (lanes past 15 repeat the last word)
+  const unsigned char* Sg = a.ks + (long long)bh * Lkp + 4 * (lane < 16 ? lane : 15);
+
+  auto issue_k = [&](int j, int stage) {
+    const unsigned char* src = Kg + (long long)j * Cfg::KT_B;
+    unsigned char* dst = smem_raw + stage * Cfg::KT_B;
+#pragma unroll
+    for (int i = 0; i < Cfg::K_DMA; ++i)
+      __builtin_amdgcn_global_load_lds(src + kdo[i], (lds_void*)(dst + (wave * Cfg::K_DMA + i) * 1024), 16, 0, 0);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(Sg + (long long)j * ATT_BN, (lds_void*)(smem_raw + Cfg::SRING + stage * Cfg::KS_B),
+                                       4, 0, 0);
+  };
+  auto issue_v = [&](int j, int stage) {
+    const unsigned char* src = Vg + (long long)j * ATT_BN * 2;
+    unsigned char* dst = smem_raw + Cfg::VRING + stage * Cfg::VT_B;
+#pragma unroll
+    for (int i = 0; i < Cfg::V_DMA; ++i)
+      __builtin_amdgcn_global_load_lds(src + vdo[i], (lds_void*)(dst + (wave * Cfg::V_DMA + i) * 1024), 16, 0, 0);
+  };
+  auto kscale = [&](int kst, int kb) -> int { return smem_raw[Cfg::SRING + kst * Cfg::KS_B + 32 * kb + l32]; };
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = -INFINITY, l = 0.f, alpha = 1.f;
+
+  // lazy running max, as in the bf16 kernel
+  auto new_max = [&](float mx) {
+    const float mnew = __builtin_elementwise_maximum(m, mx);
+    const bool mv = (mnew - m) * c > RESCALE_LOG2;
+    const float al = __builtin_amdgcn_exp2f((m - mnew) * c);
+    alpha = mv ? al : 1.0f;
+    m = mv ? mnew : m;
+    l *= alpha;
+    return __ballot(mv) != 0;
+  };
+  auto mask_block = [&](f32x16& s, int j, int kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j * ATT_BN + 32 * kb + 8 * (r / 4) + 4 * g2 + (r % 4);
+      if (key >= Lk) s[r] = -INFINITY;
+    }
+  };
+
+  // S(t) lives in S0 (keys 0..31) and S1[t % 2] (keys 32..63): the probabilities
+  // of keys 32..63 of tile t are taken while S(t+1) is computed
+  f32x16 S0, S1[2];
+  Chunk<T> pf[4];
+
+  // ---- prologue
+#pragma unroll
+  for (int j = 0; j < NR; ++j) issue_k(min(j, n - 1), j);
+#pragma unroll
+  for (int j = 0; j < NR - 1; ++j) issue_v(min(j, n - 1), j);
+  att_wait_vmcnt<0>();
+  __syncthreads();
+  {
+    const f32x16 zero = {};
+    S0 = zero;
+    S1[0] = zero;
+    const int ks0 = kscale(0, 0), ks1 = kscale(0, 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      mma8(S0, load32(smem_raw + koff[s][0], smem_raw + koff[s][1]), qf[s], ks0, qsc);
+      mma8(S1[0], load32(smem_raw + KBLK_B + koff[s][0], smem_raw + KBLK_B + koff[s][1]), qf[s], ks1, qsc);
+    }
+    if (ATT_BN > Lk) {
+      mask_block(S0, 0, 0);
+      mask_block(S1[0], 0, 1);
+    }
+    float v = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v = __builtin_elementwise_maximum(v, __builtin_elementwise_maximum(S0[r], S1[0][r]));
+    new_max(__builtin_elementwise_maximum(v, __shfl_xor(v, 32, 64)));
+    const float nmc = -m * c;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[8 * half + e], c, nmc));
+        l += p[e];
+      }
+      pack8(pf[half], p);
+    }
+  }
+  att_barrier_lds();
+
+  // One iteration, entered with S(t) and the probabilities of its keys 0..31 in
+  // pf[0..1].  20 MFMA slots, each issuing the LDS read of the operand needed 6
+  // slots later and a share of the VALU work:
+  //   slots  0..3   S(t+1) (4 fp8 MFMAs)  | probabilities of tile t, keys 32..47
+  //   slots  4..11  O += P V, keys 0..31  | probabilities of keys 48..63 (4..7);
+  //                                         masking and row maxima of S(t+1) (8..11), new max
+  //   slots 12..19  O += P V, keys 32..63 | probabilities of tile t+1, keys 0..31
+  // K_{t+1} (and its scales) sit in K stage (t+1)%2, V_t in V stage t%2; the
+  // loads issued here refill the stages read in the previous iteration.
+  auto iter = [&](int t, int ph) {
+    const int kst = (ph + 1) % NR, vst = ph;
+    issue_k(min(t + NR, n - 1), ph);
+    issue_v(min(t + NR - 1, n - 1), (ph + NR - 1) % NR);
+    const unsigned char* kbase = smem_raw + kst * Cfg::KT_B;
+    const unsigned char* vbase = smem_raw + Cfg::VRING + vst * Cfg::VT_B;
+    f32x16& Sc = S1[ph];       // S(t), keys 32..63
+    f32x16& Sn = S1[ph ^ 1];   // S(t+1), keys 32..63
+    constexpr int AHEAD = 6;
+    i32x8 kf[4];
+    Chunk<T> vf[20];
+    auto rd = [&](int i) {
+      if (i < 4)
+        kf[i] = load32(kbase + (i / 2) * KBLK_B + koff[i % 2][0], kbase + (i / 2) * KBLK_B + koff[i % 2][1]);
+      else
+        vf[i].load(vbase + ((i - 4) % 4) * VBLK_B + voff[(i - 4) / 4]);
+    };
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) rd(i);
+    const int ks0 = kscale(kst, 0), ks1 = kscale(kst, 1);
+    const bool mask_next = (t + 2) * ATT_BN > Lk;
+    float nmc = -m * c, vmax = -INFINITY, pbuf[8];
+    bool moved = false;
+#pragma unroll
+    for (int i = 0; i < 20; ++i) {
+      if (i + AHEAD < 20) rd(i + AHEAD);
+      if (i < 4) {
+        const int kb = i / 2, s = i % 2;
+        if (s == 0) {
+          const f32x16 zero = {};
+          if (kb == 0) S0 = zero; else Sn = zero;
+        }
+        if (kb == 0) mma8(S0, kf[i], qf[s], ks0, qsc);
+        else mma8(Sn, kf[i], qf[s], ks1, qsc);
+      } else {
+        const int u = (i - 4) / 4, db = (i - 4) % 4;
+        mma32(o[db], vf[i], pf[u]);
+      }
+      if (i < 8) {
+        // probabilities of tile t, keys 32..63: elements 2i, 2i+1 of Sc
+#pragma unroll
+        for (int e = 2 * i; e < 2 * i + 2; ++e) {
+          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[e], c, nmc));
+          l += pbuf[e % 8];
+        }
+        if (i % 4 == 3) {
+          pack8(pf[2 + i / 4], pbuf);
+          asm volatile("" : "+v"(pf[2 + i / 4].v), "+v"(l));
+        }
+      } else if (i < 12) {
+        // row maxima of S(t+1): keys 0..31 in slots 8, 9; keys 32..63 in slots 10, 11
+        const int kb = (i - 8) / 2, k = (i - 8) % 2;
+        f32x16& Sb = kb == 0 ? S0 : Sn;
+        if (k == 0 && mask_next) mask_block(Sb, t + 1, kb);
+#pragma unroll
+        for (int r = 8 * k; r < 8 * k + 8; r += 2)
+          vmax = __builtin_elementwise_maximum(vmax, __builtin_elementwise_maximum(Sb[r], Sb[r + 1]));
+        asm volatile("" : "+v"(vmax));
+        if (i == 11) {
+          moved = new_max(__builtin_elementwise_maximum(vmax, __shfl_xor(vmax, 32, 64)));
+          nmc = -m * c;
+          asm volatile("" : "+v"(m), "+v"(l), "+v"(alpha), "+v"(nmc));
+        }
+      } else {
+        // probabilities of tile t+1, keys 0..31: elements 2(i-12), +1 of S0
+#pragma unroll
+        for (int e = 2 * (i - 12); e < 2 * (i - 12) + 2; ++e) {
+          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], c, nmc));
+          l += pbuf[e % 8];
+        }
+        if (i % 4 == 3) {
+          pack8(pf[(i - 12) / 4], pbuf);
+          asm volatile("" : "+v"(pf[(i - 12) / 4].v), "+v"(l));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (moved) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    att_wait_vmcnt<0>();  // K_{t+2} (with scales) and V_{t+1} have landed
+    att_barrier_lds();
+  };
+  for (int t = 0; t < n; t += 2) {
+    iter(t, 0);
+    if (t + 1 < n) iter(t + 1, 1);
+  }
+  att_wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- epilogue: normalise, stage the wave's 32 rows in LDS as [query][d], 16-byte row stores
+  constexpr int HC = HD / 8;
+  T* stg = reinterpret_cast<T*>(smem_raw) + wave * (32 * HD);
+  {
+    const float inv = 1.0f / (l + __shfl_xor(l, 32, 64));
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r / 4) + 4 * g2 + (r % 4);
+        stg[l32 * HD + d] = from_f<T>(o[db][r] * inv);
+      }
+  }
+  __syncthreads();
+  const int ld = a.heads * HD;
+#pragma unroll
+  for (int u = 0; u < (32 * HC) / 64; ++u) {
+    const int idx = lane + 64 * u;
+    const int qr = idx / HC, cc = idx % HC;
+    const int q = q0 + qr;
+    if (q < a.Lq) {
+      Chunk<T> v;
+      v.load(stg + qr * HD + cc * 8);
+      v.store(reinterpret_cast<T*>(a.o) + ((long long)b * a.Lq + q) * ld + h * HD + cc * 8);
+    }
+  }
+}
+
 // Kernel entry points (thin wrappers: the host pass only sees these).  Self- and
 // text cross-attention run the same body under two symbols so that traces
 // separate them; KIND only keeps the instantiations apart.
@@ -745,6 +1082,11 @@ __global__ __launch_bounds__(256, 2) void attn_cross_kernel(const AttnArgs a) {
 template <int HD, int NR, int QB, int NW>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && QB == 1) ? 2 : 1) void attn_self_wide_kernel(const AttnArgs a) {
   attn_wide_body<HD, NR, QB, NW>(a);
+}
+// bf16 self-attention with 8-bit scores: 8 waves of 32 queries, one workgroup per CU
+template <int NR, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_self_qk8_kernel(const AttnArgs a) {
+  attn_wide8_body<NR, NW>(a);
 }
 // image + text sources keep a second accumulator: one workgroup per CU
 template <typename T, int HD>
@@ -789,9 +1131,33 @@ hipError_t launch_attn_wide(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int NR, int NW>
+hipError_t launch_attn_qk8(const AttnArgs& a, hipStream_t st) {
+  using Cfg = Wide8Cfg<NR, NW>;
+  auto kern = attn_self_qk8_kernel<NR, NW>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nqt = (a.Lq + Cfg::BMQ - 1) / Cfg::BMQ;
+  const int G = nqt * a.heads * a.B;
+  hipLaunchKernelGGL(kern, dim3(G), dim3(64 * NW), Cfg::LDS_BYTES, st, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.Lq <= 0) return hipSuccess;
+  if (a.qk8) {
+    // 8-bit scores: bf16 V, one key source, 128-wide heads, padded key rows
+    if (sizeof(T) != 2 || a.hd != 128 || a.nsrc != 1 || !a.qs || !a.ks || a.Lk[0] < 1 || a.Lkp[0] % ATT_BN != 0 ||
+        a.Lkp[0] < a.Lk[0])
+      return hipErrorInvalidValue;
+    if constexpr (sizeof(T) == 2) return launch_attn_qk8<2, 8>(a, st);
+  }
   if constexpr (sizeof(T) == 2) {
     if (a.hd == 128 && a.nsrc == 1 && a.self) return launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW>(a, st);
   }

@@ -44,7 +44,8 @@ struct Gemm {
   static constexpr size_t SLAB_BYTES = (size_t)BM * SWP * 4;
   // the v^T section of a packing GEMM stages its slab transposed ([column][row])
   static constexpr int SWPT = BM + 8;
-  static constexpr size_t SLABT_BYTES = EPI == EPI_PACK ? (size_t)SW * SWPT * 4 : 0;
+  static constexpr bool PACK = EPI == EPI_PACK || EPI == EPI_PACK8;
+  static constexpr size_t SLABT_BYTES = PACK ? (size_t)SW * SWPT * 4 : 0;
   static constexpr size_t SLAB_MAX = SLAB_BYTES > SLABT_BYTES ? SLAB_BYTES : SLABT_BYTES;
   static constexpr size_t LDS_BYTES = PIPE_BYTES > SLAB_MAX ? PIPE_BYTES : SLAB_MAX;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -365,7 +366,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // multiple of BM): the slab is staged transposed, so that a lane reads 8
   // tokens of one feature column as two 16-byte LDS reads and writes them as
   // one 16-byte store
-  const bool vt_tile = EPI == EPI_PACK && n0 >= g.nq + g.nk && g.c_rpb % BM == 0;
+  constexpr bool PACK = C::PACK;
+  // 8-bit q / k: the 16 lanes that hold one token row of a slab hold one whole head
+  static_assert(EPI != EPI_PACK8 || SW % 128 == 0, "8-bit q / k need head-aligned slabs");
+  const bool vt_tile = PACK && n0 >= g.nq + g.nk && g.c_rpb % BM == 0;
 #pragma unroll
   for (int s0 = 0; s0 < BN; s0 += SW) {
     // phase 1: the accumulators hold C^T (the weight fragment is the MFMA row
@@ -382,7 +386,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
             const int row = arow0 + 32 * i + l32;
-            if (EPI == EPI_PACK && vt_tile) {
+            if (PACK && vt_tile) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) slab[(col + e) * SWPT + row] = acc[i][j][4 * rq + e];
             } else {
@@ -398,8 +402,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     // phase 2
     const int nbase = n0 + s0;
     int sec = 0;
-    if (EPI == EPI_PACK) sec = nbase < g.nq ? 0 : (nbase < g.nq + g.nk ? 1 : 2);
-    if (EPI == EPI_PACK && vt_tile) {
+    if (PACK) sec = nbase < g.nq ? 0 : (nbase < g.nq + g.nk ? 1 : 2);
+    if (PACK && vt_tile) {
       // v^T from the transposed slab.  Lane work item (column, 16-token group,
       // half hf): tokens 4hf..4hf+3 and 8+4hf..8+4hf+3 of the group, which the
       // key permutation stores at positions 8hf..8hf+7 -- one 16-byte store;
@@ -438,7 +442,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
         }
       }
-    } else if (EPI == EPI_PACK && sec == 2) {
+    } else if (PACK && sec == 2) {
       // v^T: a chunk is 8 consecutive tokens of one feature column
       const int nv0 = nbase - g.nq - g.nk;
       for (int idx = tid; idx < SW * (BM / 8); idx += NT) {
@@ -530,7 +534,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
           *reinterpret_cast<f32x4*>(xp) = x0;
           *reinterpret_cast<f32x4*>(xp + 4) = x1;
-        } else if (EPI == EPI_PACK) {
+        } else if (PACK) {
           // q or k, with optional RoPE on the adjacent pairs of the chunk
           const int nsec = n - (sec == 0 ? 0 : g.nq);
           const int hh = nsec / g.hd, e0 = nsec - hh * g.hd;
@@ -548,10 +552,35 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
               v[u + 1] = u0 * cs[u + 1] + u1 * cs[u];
             }
           }
-          Chunk<T> c;
-          pack8(c, v);
-          T* base = reinterpret_cast<T*>(sec == 0 ? g.q : g.k);
-          c.store(base + (((long long)b * g.heads + hh) * g.Lp + t) * g.hd + e0);
+          const long long rowidx = ((long long)b * g.heads + hh) * g.Lp + t;
+          if constexpr (EPI == EPI_PACK8) {
+            // e4m3 with one power-of-two scale per (token, head): 2^e with the
+            // smallest e (clamped to [-127, 127]) that brings max|row| to 448 or
+            // below, stored as the E8M0 byte e + 127.  max|row| gathers over the
+            // 16 lanes of the head; frexp(amax) = m 2^E gives e = E - 9 + (m > 7/8).
+            float am = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) am = __builtin_elementwise_maximum(am, fabsf(v[u]));
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) am = __builtin_elementwise_maximum(am, __shfl_xor(am, o, 64));
+            const unsigned ab = __float_as_uint(am);
+            const int ef = (int)(ab >> 23);
+            int ex = ef == 0 ? (am == 0.f ? 0 : -127) : ef - 135 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+            ex = ex < -127 ? -127 : ex;
+            const float inv = __uint_as_float((unsigned)(127 - ex) << 23);  // 2^-e, exact scaling
+            unsigned w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * inv, v[1] * inv, 0u, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * inv, v[3] * inv, w0, true);
+            unsigned w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * inv, v[5] * inv, 0u, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * inv, v[7] * inv, w1, true);
+            unsigned char* base = reinterpret_cast<unsigned char*>(sec == 0 ? g.q : g.k);
+            *reinterpret_cast<uint2*>(base + rowidx * g.hd + e0) = make_uint2(w0, w1);
+            if (e0 == 0) (sec == 0 ? g.qs : g.ks)[rowidx] = (unsigned char)(ex + 127);
+          } else {
+            Chunk<T> c;
+            pack8(c, v);
+            T* base = reinterpret_cast<T*>(sec == 0 ? g.q : g.k);
+            c.store(base + rowidx * g.hd + e0);
+          }
         }
       }
     }
@@ -624,6 +653,13 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
     case EPI_STORE_F32: return launch_by_n<T, LOAD_PLAIN, EPI_STORE_F32>(g, st);
     case EPI_RESID: return launch_by_n<T, LOAD_PLAIN, EPI_RESID>(g, st);
     case EPI_PACK: return launch_by_n<T, LOAD_PLAIN, EPI_PACK>(g, st);
+    case EPI_PACK8:
+      // 8-bit q / k need whole heads of 128 in one 128-column slab: 256x256 tiles only
+      if constexpr (sizeof(T) == 2) {
+        if (g.N % 256 != 0 || g.hd != 128 || !g.qs || !g.ks) return hipErrorInvalidValue;
+        return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_PLAIN, EPI_PACK8>(g, st);
+      }
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

@@ -7,7 +7,7 @@
 namespace wan {
 
 enum Loader { LOAD_PLAIN = 0, LOAD_PATCH = 1 };
-enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_STORE_F32 = 2, EPI_RESID = 3, EPI_PACK = 4 };
+enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_STORE_F32 = 2, EPI_RESID = 3, EPI_PACK = 4, EPI_PACK8 = 5 };
 
 // C[M][N] = A[M][K] * W[N][K]^T + bias, with an epilogue selected by `epi`.
 struct GemmArgs {
@@ -39,10 +39,14 @@ struct GemmArgs {
   long long ldx = 0;
   const float* gate = nullptr;
   long long gate_bstride = 0;
-  // EPI_PACK: columns [0, nq) -> q, [nq, nq+nk) -> k, rest -> v^T; all head-major
+  // EPI_PACK: columns [0, nq) -> q, [nq, nq+nk) -> k, rest -> v^T; all head-major.
+  // EPI_PACK8 (bf16, hd == 128): q and k as e4m3 bytes [B][H][Lp][hd] plus one
+  // scale byte per (batch, head, token) in qs / ks [B][H][Lp]; v^T as EPI_PACK
   void* q = nullptr;
   void* k = nullptr;
   void* vt = nullptr;
+  unsigned char* qs = nullptr;
+  unsigned char* ks = nullptr;
   int nq = 0, nk = 0;
   int heads = 1, hd = 128, Lp = 64;
   const float2* rope = nullptr;  // per-token (cos, sin) table [token][hd/2], or NULL for no rotation
@@ -61,6 +65,11 @@ struct AttnArgs {
   int Lk[2] = {0, 0}, Lkp[2] = {0, 0};
   int nsrc = 1;
   int self = 0;  // 1: self-attention (selects the kernel symbol; the computation is the same)
+  // qk8 (bf16, self, hd == 128): q and k are e4m3 bytes with per-row scale bytes qs [B][H][Lqp]
+  // and ks [B][H][Lkp] (power-of-two exponent + 127), as EPI_PACK8 writes them
+  int qk8 = 0;
+  const unsigned char* qs = nullptr;
+  const unsigned char* ks = nullptr;
   void* o = nullptr;
   int B = 1, heads = 1, hd = 128;
   float scale_log2 = 0.f;

@@ -39,6 +39,7 @@ class WanConfig:
     img_len: int = 0
     n_blocks: int = 1
     mode: str = "fp32"       # "fp32" or "bf16"
+    qk8: bool = False        # bf16 only: self-attention scores from 8-bit q and k
     timestep: float = 500.0
     dt: float = 0.05
     guide_scale: float = 5.0
