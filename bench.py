@@ -150,6 +150,7 @@ def main():
     ap.add_argument("--config", default="wan13b_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-modes", action="store_true", help="skip timing the diffusion-cache step modes")
+    ap.add_argument("--no-qk8", action="store_true", help="skip timing the step with 8-bit self-attention scores")
     ap.add_argument("--block-configs", default="",
                     help="comma-separated block configurations to time one block forward of "
                          "(e.g. wan13b_block,wan14b_720p_block,wan14b_i2v_block); reported under 'blocks'")
@@ -205,6 +206,26 @@ def main():
                                            ("cross_attention", N.KERNEL_CROSS_ATTENTION),
                                            ("gemm", N.KERNEL_GEMM), ("elementwise", N.KERNEL_ELEMENTWISE))}
     assert bool(torch.isfinite(z).all())
+    # the same step with 8-bit self-attention scores (WAN_BF16_QK8; same weights)
+    qk8 = None
+    if not args.no_qk8:
+        cfg8 = cfg.with_(qk8=True)
+        z8 = z0.clone()
+        W.denoise_step(cfg8, model, z8, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws)
+        torch.cuda.synchronize()
+        W.timing_enable(True)
+        W.timing_read(N.KERNEL_SELF_ATTENTION, reset=True)
+        t1 = time.perf_counter()
+        for _ in range(3):
+            W.denoise_step(cfg8, model, z8, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws)
+        torch.cuda.synchronize()
+        ms8 = (time.perf_counter() - t1) / 3 * 1e3
+        W.timing_enable(False)
+        a8_ms, a8_n = W.timing_read(N.KERNEL_SELF_ATTENTION)
+        assert bool(torch.isfinite(z8).all())
+        qk8 = {"ms_per_step": round(ms8, 3), "self_attention_ms_per_step": round(a8_ms / 3, 3),
+               "self_attention_avg_launch_ms": round(a8_ms / max(a8_n, 1), 4)}
+        del z8
     # diffusion cache: one step in each mode (after a store step), timed alone
     cache_ms = None
     if not args.no_cache_modes:
@@ -277,6 +298,15 @@ def main():
                      "avg_launch_ms": round(attn_avg, 4), "launches": attn_n,
                      "flop_per_launch": bf["self_attention"]},
     }
+    if qk8 is not None:
+        a8 = qk8["self_attention_avg_launch_ms"]
+        qk8.update({
+            "tflops_equivalent": round(flops / (qk8["ms_per_step"] * 1e-3) / 1e12, 2),
+            "speedup_vs_bf16_step": round(ms_step / qk8["ms_per_step"], 4),
+            "self_attention_speedup": round(attn_avg / a8, 4) if a8 > 0 else None,
+            "note": "same step with self-attention scores from e4m3 q and k (per-token power-of-two scales); "
+                    "P V, GEMMs and the rest stay bf16; reduced-precision variant, not the headline value"})
+        out["qk8_step"] = qk8
     if cache_ms is not None:
         out["diffusion_cache"] = {
             "ms_per_step": cache_ms, "cache_gb": cache_gb,
