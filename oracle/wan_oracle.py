@@ -228,12 +228,14 @@ def quantize_rows_e4m3(x):
     """8-bit form of q or k ([P2] method: FP8 GEMM and 8-bit FlashAttention at
     inference; the scaling rule is this build's reading): every row (one token of
     one head) is rounded to float32, given the power-of-two scale 2^e with the
-    smallest e such that max|row| / 2^e <= 448, and rounded to e4m3 in that scale.
+    smallest e such that max|row| / 2^e <= 448 (clamped to [-127, 127]), and
+    rounded to e4m3 in that scale.
     Returns the dequantized rows (float64) and the exponents e."""
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     amax = np.abs(x32).max(axis=-1)
     mant, ex = np.frexp(amax)           # amax = mant * 2^ex, mant in [0.5, 1)
     e = np.where(amax > 0, ex - 9 + (mant > 0.875), 0).astype(np.int64)
+    e = np.clip(e, -127, 127)            # the range of an 8-bit power-of-two scale (exponent + 127)
     scale = np.exp2(e.astype(np.float64))[..., None]
     return e4m3_round(x32 / scale) * scale, e
 
@@ -244,6 +246,27 @@ def round_bf16_rne(a):
     u = np.asarray(a, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
     u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+FP8_BLOCK = 128
+
+
+def quantize_blocks_e4m3(x, block=FP8_BLOCK):
+    """8-bit form of a GEMM operand ([P2] method: FP8 GEMMs at inference; the
+    scaling rule is this build's reading): each row is cut into blocks of
+    `block` consecutive elements along the contraction axis, and every block is
+    quantised as one row of quantize_rows_e4m3 (its own power-of-two scale,
+    e4m3 values).  Returns the dequantised operand (float64)."""
+    x = f64(x)
+    shp = x.shape
+    q, _ = quantize_rows_e4m3(x.reshape(shp[:-1] + (shp[-1] // block, block)))
+    return q.reshape(shp)
+
+
+def linear_fp8(x, w, b):
+    """x W^T + b with both operands in their 8-bit form (blocks of 128 along the
+    contraction axis: per token for x, per output feature for W)."""
+    return quantize_blocks_e4m3(x) @ quantize_blocks_e4m3(w).T + f64(b)
 
 
 def attention_qk8(q, k, v, chunk=4096):
@@ -272,7 +295,7 @@ def _lin(x, w, b):
     return f64(x) @ f64(w).T + f64(b)
 
 
-def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8=False):
+def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8=False, fp8=False):
     """Self-attention sublayer output (before its gate).
 
     q, k, v = m W_qkv^T + b_qkv (rows of W_qkv ordered [q; k; v]); RoPE on q and
@@ -286,7 +309,10 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8
     rounding is a decision taken on q and k, so it is taken on the values the
     library decides on: q and k projected from the bfloat16 form of m (the
     operand precision of the projection in bf16 mode), see round_bf16_rne.
+    fp8: the q, k, v projection is an 8-bit GEMM (linear_fp8); q and k are then
+    decided on as that GEMM gives them (implies qk8).
     """
+    qk8 = qk8 or fp8
     if attn is not None:
         a = f64(attn) if rows is None else f64(attn)[:, rows]
         return _lin(a, w["o_w"], w["o_b"])
@@ -294,19 +320,20 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8
     d = D // heads
     wq, wk, wv = np.split(f64(w["qkv_w"]), 3, axis=0)
     bq, bk, bv = np.split(f64(w["qkv_b"]), 3)
-    m_qk = round_bf16_rne(m_all) if qk8 else m_all
-    k = rope_apply(_lin(m_qk, wk, bk).reshape(B, L, heads, d), grid).reshape(B, L, D)
-    v = _lin(m_all, wv, bv)
+    lin = linear_fp8 if fp8 else _lin
+    m_qk = round_bf16_rne(m_all) if qk8 and not fp8 else m_all
+    k = rope_apply(lin(m_qk, wk, bk).reshape(B, L, heads, d), grid).reshape(B, L, D)
+    v = lin(m_all, wv, bv)
     mq = m_qk if rows is None else m_qk[:, rows]
     n = mq.shape[1]
-    q = rope_apply(_lin(mq, wq, bq).reshape(B, n, heads, d), grid, rows).reshape(B, n, D)
+    q = rope_apply(lin(mq, wq, bq).reshape(B, n, heads, d), grid, rows).reshape(B, n, D)
     a = multihead_attention(q, k, v, heads, qk8)
     if record is not None:
         record.append(a)
     return _lin(a, w["o_w"], w["o_b"])
 
 
-def cross_attention(xn, ctx, w, heads, img_len):
+def cross_attention(xn, ctx, w, heads, img_len, fp8=False):
     """Cross-attention to the context tokens (ungated, un-modulated).
 
     [P2] method: text conditions enter through cross-attention.  [P3] core code:
@@ -315,8 +342,10 @@ def cross_attention(xn, ctx, w, heads, img_len):
     one shared query projection, separate K/V projections and separate softmax
     for the image tokens and the text tokens, the two results summed before the
     shared output projection.
+    fp8: the query projection is an 8-bit GEMM (linear_fp8); the context K / V
+    projections and the output projection stay exact.
     """
-    q = _lin(xn, w["cq_w"], w["cq_b"])
+    q = (linear_fp8 if fp8 else _lin)(xn, w["cq_w"], w["cq_b"])
     ctx = f64(ctx)
     D = ctx.shape[-1]
     ctx_img, ctx_txt = ctx[:, :img_len], ctx[:, img_len:]
@@ -328,12 +357,13 @@ def cross_attention(xn, ctx, w, heads, img_len):
     return _lin(a, w["co_w"], w["co_b"])
 
 
-def ffn(xm, w):
-    """GELU feed-forward: W2 GELU(W1 m + b1) + b2."""
-    return _lin(gelu(_lin(xm, w["ff1_w"], w["ff1_b"])), w["ff2_w"], w["ff2_b"])
+def ffn(xm, w, fp8=False):
+    """GELU feed-forward: W2 GELU(W1 m + b1) + b2 (fp8: both as 8-bit GEMMs, linear_fp8)."""
+    lin = linear_fp8 if fp8 else _lin
+    return lin(gelu(lin(xm, w["ff1_w"], w["ff1_b"])), w["ff2_w"], w["ff2_b"])
 
 
-def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, record=None, qk8=False):
+def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, record=None, qk8=False, fp8=False):
     """One DiT block, residual stream in float64.
 
         x <- x + g1 * SA(LN(x) (1 + sc1) + sh1)
@@ -344,7 +374,8 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
     scale2, gate2); ctx: (B, L_img + L_txt, D).
     rows: if given, return only those tokens' outputs (the keys and values of
     self-attention still come from every token) -> (B, len(rows), D).
-    attn / record: see self_attention (diffusion cache); qk8: 8-bit q k^T in self-attention.
+    attn / record: see self_attention (diffusion cache); qk8: 8-bit q k^T in self-attention;
+    fp8: the q/k/v, cross-attention query and both FFN projections as 8-bit GEMMs, plus qk8.
     """
     x = f64(x)
     mod = f64(mod)
@@ -353,9 +384,9 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
     sh1, sc1, g1, sh2, sc2, g2 = [mod[:, i][:, None, :] for i in range(6)]
     m_all = modulate(layer_norm(x), sh1, sc1)
     xr = x if rows is None else x[:, rows]
-    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record, qk8)
-    xr = xr + cross_attention(layer_norm(xr), ctx, w, heads, img_len)
-    xr = xr + g2 * ffn(modulate(layer_norm(xr), sh2, sc2), w)
+    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record, qk8, fp8)
+    xr = xr + cross_attention(layer_norm(xr), ctx, w, heads, img_len, fp8)
+    xr = xr + g2 * ffn(modulate(layer_norm(xr), sh2, sc2), w, fp8)
     return xr
 
 
@@ -381,7 +412,8 @@ def euler_update(z, v, dt):
     return f64(z) + dt * f64(v)
 
 
-def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0, attn_cache=None, record=None, qk8=False):
+def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0, attn_cache=None, record=None, qk8=False,
+                fp8=False):
     """Velocity prediction of the whole DiT for one context: (B, 16, F, H, W).
 
     attn_cache: per-block cached self-attention outputs to use instead of
@@ -394,16 +426,16 @@ def dit_forward(z, cond, ctx, model_w, blocks_w, heads, tau, img_len=0, attn_cac
                           model_w["t2_b"], model_w["m_w"], model_w["m_b"])
     for i, w in enumerate(blocks_w):
         x = dit_block(x, mod, ctx, w, heads, grid, img_len,
-                      attn=None if attn_cache is None else attn_cache[i], record=record, qk8=qk8)
+                      attn=None if attn_cache is None else attn_cache[i], record=record, qk8=qk8, fp8=fp8)
     p = head(x, model_w["hd_w"], model_w["hd_b"])
     return patch_scatter(p, F, H, W)
 
 
 def denoise_step(z, cond, ctx_cond, ctx_null, model_w, blocks_w, heads, tau, dt,
-                 guide_scale, img_len=0, qk8=False):
+                 guide_scale, img_len=0, qk8=False, fp8=False):
     """One CFG denoise step: both branches, guidance combine, Euler update."""
-    v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len, qk8=qk8)
-    v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len, qk8=qk8)
+    v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len, qk8=qk8, fp8=fp8)
+    v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len, qk8=qk8, fp8=fp8)
     return euler_update(z, cfg_combine(v_c, v_u, guide_scale), dt)
 
 
@@ -414,7 +446,7 @@ CACHE_REUSE_UNCOND = 4
 
 
 def denoise_step_cached(z, cond, ctx_cond, ctx_null, model_w, blocks_w, heads, tau, dt,
-                        guide_scale, mode, cache, img_len=0):
+                        guide_scale, mode, cache, img_len=0, qk8=False, fp8=False):
     """One CFG denoise step with the diffusion cache ([P2] method: inference reuses
     the similarity of attention between sampling steps and of the two CFG
     branches; the pages give no further rule, the reading taken is):
@@ -431,18 +463,20 @@ def denoise_step_cached(z, cond, ctx_cond, ctx_null, model_w, blocks_w, heads, t
     """
     if mode == CACHE_STORE:
         rec_c, rec_u = [], []
-        v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len, record=rec_c)
-        v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len, record=rec_u)
+        v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len, record=rec_c,
+                          qk8=qk8, fp8=fp8)
+        v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len, record=rec_u,
+                          qk8=qk8, fp8=fp8)
         cache["attn_c"], cache["attn_u"], cache["v_u"] = rec_c, rec_u, v_u
     else:
         if mode & ~(CACHE_REUSE_ATTN | CACHE_REUSE_UNCOND) or mode == 0:
             raise ValueError(f"cache mode {mode}")
         reuse_attn = bool(mode & CACHE_REUSE_ATTN)
         v_c = dit_forward(z, cond, ctx_cond, model_w, blocks_w, heads, tau, img_len,
-                          attn_cache=cache["attn_c"] if reuse_attn else None)
+                          attn_cache=cache["attn_c"] if reuse_attn else None, qk8=qk8, fp8=fp8)
         if mode & CACHE_REUSE_UNCOND:
             v_u = cache["v_u"]
         else:
             v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len,
-                              attn_cache=cache["attn_u"] if reuse_attn else None)
+                              attn_cache=cache["attn_u"] if reuse_attn else None, qk8=qk8, fp8=fp8)
     return euler_update(z, cfg_combine(v_c, v_u, guide_scale), dt)

@@ -630,3 +630,71 @@ def test_qk8_self_attention_decides_on_the_bf16_activation():
     w_v0["qkv_b"][2 * D:] = 1.0                                 # v = 1 everywhere: output 1 for any weights
     O.self_attention(m + tiny, w_v0, heads, grid, qk8=True, record=rec_b)
     np.testing.assert_allclose(rec_b[0], 1.0, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- 8-bit GEMM operands
+def test_block_quantisation_is_rowwise_quantisation_of_each_block():
+    """Blocks of 128 along the last axis are independent rows of the per-row rule: changing one
+    block leaves the others' rounded values alone, and a row of one block equals the row rule."""
+    x = rng.standard_normal((5, 384)) * np.exp2(rng.integers(-6, 6, (5, 1)))
+    q = O.quantize_blocks_e4m3(x)
+    for b in range(3):
+        sl = slice(128 * b, 128 * (b + 1))
+        np.testing.assert_array_equal(q[:, sl], O.quantize_rows_e4m3(x[:, sl])[0])
+    y = x.copy()
+    y[:, 128:256] *= 1000.0
+    np.testing.assert_array_equal(O.quantize_blocks_e4m3(y)[:, :128], q[:, :128])
+    np.testing.assert_array_equal(O.quantize_blocks_e4m3(y)[:, 256:], q[:, 256:])
+
+
+def test_scale_exponent_clamp():
+    """Rows whose largest magnitude needs an exponent below -127 take -127 (the scale byte's range)."""
+    x = np.array([[2.0 ** -130, 2.0 ** -131], [3.0 * 2.0 ** -120, 0.0]])
+    _, e = O.quantize_rows_e4m3(x)
+    assert e[0] == -127 and e[1] == max(-127, int(np.frexp(3.0 * 2.0 ** -120)[1]) - 9)
+    # with the clamp the tiny row is still rounded on the e4m3 grid of 2^-127 (its values are
+    # subnormal e4m3 multiples of 2^-136 after scaling)
+    q, _ = O.quantize_rows_e4m3(x)
+    np.testing.assert_array_equal(q[0], np.round(x[0] / 2.0 ** -136) * 2.0 ** -136)
+
+
+def test_linear_fp8_exact_on_representable_operands():
+    """Operands whose 128-blocks are already e4m3 multiples of a power of two that reaches 448
+    are left unchanged, so the 8-bit GEMM equals the exact one; random operands land within
+    the e4m3 rounding bound."""
+    grid = _e4m3_grid()
+    vals = np.concatenate([grid, -grid])
+    x = rng.choice(vals, (7, 256)) * 2.0 ** -5
+    w = rng.choice(vals, (9, 256)) * 2.0 ** 3
+    x[:, ::128] = 448.0 * 2.0 ** -5                        # every block reaches its scale's top
+    w[:, ::128] = -448.0 * 2.0 ** 3
+    b = rng.standard_normal(9)
+    np.testing.assert_allclose(O.linear_fp8(x, w, b), x @ w.T + b, rtol=1e-13, atol=1e-9)
+    x = rng.standard_normal((30, 512))
+    w = rng.standard_normal((20, 512)) * 0.02
+    ref = x @ w.T
+    err = np.linalg.norm(O.linear_fp8(x, w, np.zeros(20)) - ref) / np.linalg.norm(ref)
+    assert 1e-3 < err < 6e-2
+
+
+def test_fp8_block_reduces_to_the_exact_block_on_representable_weights_and_switches_sublayers():
+    """dit_block(fp8=True) differs from the exact block only through the 8-bit projections: with
+    every gate and W_co zero it is the identity, and an FFN-only block equals the FFN through
+    linear_fp8 written out."""
+    from video_diffusion_transformer_forward_amd import synth as S
+    cfg = S.get_config("toy").with_(heads=2)
+    w = S.block_weights(cfg, 0)
+    x = S.block_inputs(cfg)
+    mod = S.modulation(cfg)
+    ctx = S.context(cfg, "cond")
+    m = mod.copy()
+    m[:, 2] = 0.0
+    ww = dict(w, co_w=np.zeros_like(w["co_w"]), co_b=np.zeros_like(w["co_b"]))
+    # FFN only
+    out = O.dit_block(x, m, ctx, ww, cfg.heads, cfg.grid, fp8=True)
+    mm = O.modulate(O.layer_norm(np.asarray(x, np.float64)), m[:, 3][:, None, :], m[:, 4][:, None, :])
+    h = O.gelu(O.linear_fp8(mm, w["ff1_w"], w["ff1_b"]))
+    ref = x + m[:, 5][:, None, :] * O.linear_fp8(h, w["ff2_w"], w["ff2_b"])
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    m[:, 5] = 0.0
+    np.testing.assert_array_equal(O.dit_block(x, m, ctx, ww, cfg.heads, cfg.grid, fp8=True), x)
