@@ -61,6 +61,18 @@ extern "C" {
  * probabilities and v stay bf16, cross-attention is unchanged.  Needs
  * dim / heads == 128 (WAN_E_SHAPE otherwise). */
 #define WAN_BF16_QK8 2
+/* As WAN_BF16_QK8, and the q/k/v projection, the cross-attention query
+ * projection and both FFN projections are 8-bit GEMMs ([P2] method: FP8 GEMMs
+ * at inference; the scaling rule is this library's reading): both operands
+ * are cut into blocks of 128 consecutive elements along the contraction axis
+ * (per token for the activation, per output feature for the weight), each
+ * block gets the power-of-two scale and e4m3 rounding of WAN_BF16_QK8, and the
+ * products accumulate in float32.  The weights stay bf16 at the interface and
+ * are quantised inside each call.  The self- and cross-attention output
+ * projections and the context K / V projections stay bf16.  Needs
+ * dim / heads == 128 (WAN_E_SHAPE otherwise); the workspace is larger than in
+ * bf16 mode (wan_workspace_bytes). */
+#define WAN_FP8 3
 
 /* entry ids for wan_workspace_bytes */
 #define WAN_ENTRY_PATCHIFY 0

@@ -76,7 +76,7 @@ def gpu_block(cfg, w, x, mod, ctx, mod_stride=None):
 
 
 def oracle_block(cfg, w, x, mod, ctx, rows=None):
-    return O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, cfg.img_len, rows=rows, qk8=cfg.qk8)
+    return O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, cfg.img_len, rows=rows, qk8=cfg.qk8, fp8=cfg.fp8)
 
 
 def block_case(cfg, zero_co=False):

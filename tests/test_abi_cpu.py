@@ -177,3 +177,21 @@ def test_qk8_mode_shapes():
     assert st.value == N.WAN_E_SHAPE
     with pytest.raises(ValueError):
         shape_of(get_config("toy").with_(qk8=True))                    # fp32 has no 8-bit form
+
+
+def test_fp8_mode_shapes():
+    """8-bit GEMM mode: a larger workspace than bf16 (e4m3 activations, weights and scales) for
+    128-wide heads, WAN_E_SHAPE for 64-wide heads."""
+    lib = N.load()
+    st = ctypes.c_int(0)
+    cfg = get_config("wan13b_step")
+    sizes = {}
+    for k, kw in (("bf16", {}), ("fp8", dict(fp8=True))):
+        sh = shape_of(cfg.with_(**kw))
+        sizes[k] = lib.wan_workspace_bytes(ctypes.byref(sh), N.ENTRY_STEP, ctypes.byref(st))
+        assert st.value == N.WAN_OK
+    D, F, L = cfg.dim, cfg.ffn_dim, cfg.seq_len
+    assert sizes["fp8"] - sizes["bf16"] >= 2 * L * F + 4 * D * D + 2 * F * D
+    sh = shape_of(get_config("toy").with_(mode="bf16", fp8=True))
+    assert lib.wan_workspace_bytes(ctypes.byref(sh), N.ENTRY_BLOCK, ctypes.byref(st)) == 0
+    assert st.value == N.WAN_E_SHAPE

@@ -35,9 +35,11 @@ def shape_of(cfg: WanConfig) -> N.WanShape:
 
 def _mode_id(cfg: WanConfig) -> int:
     if cfg.mode == "bf16":
+        if cfg.fp8:
+            return N.WAN_FP8
         return N.WAN_BF16_QK8 if cfg.qk8 else N.WAN_BF16
-    if cfg.qk8:
-        raise ValueError("8-bit q k^T needs mode 'bf16'")
+    if cfg.qk8 or cfg.fp8:
+        raise ValueError("the 8-bit forms need mode 'bf16'")
     return N.WAN_FP32
 
 

@@ -19,6 +19,7 @@ WAN_E_ENTRY = -7
 WAN_BF16 = 0
 WAN_FP32 = 1
 WAN_BF16_QK8 = 2
+WAN_FP8 = 3
 
 ENTRY_PATCHIFY = 0
 ENTRY_BLOCK = 1

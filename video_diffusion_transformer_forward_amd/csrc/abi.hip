@@ -28,20 +28,21 @@ int pad256(int x) { return (x + 255) / 256 * 256; }
 
 struct Dims {
   int B, Cin, F, H, W, Hh, Ww, L, Lp, D, heads, hd, Ff, Lt, Li, Lc, Ltp, Lip, mode;
-  bool qk8;  // self-attention scores from 8-bit q and k (WAN_BF16_QK8)
+  bool qk8;  // self-attention scores from 8-bit q and k (WAN_BF16_QK8, WAN_FP8)
+  bool fp8;  // 8-bit projections (WAN_FP8)
   size_t es;
 };
 
 int check_shape(const wan_shape* s, Dims* d) {
   if (!s) return WAN_E_NULL;
-  if (s->mode != WAN_BF16 && s->mode != WAN_FP32 && s->mode != WAN_BF16_QK8) return WAN_E_MODE;
+  if (s->mode != WAN_BF16 && s->mode != WAN_FP32 && s->mode != WAN_BF16_QK8 && s->mode != WAN_FP8) return WAN_E_MODE;
   if (s->batch < 1 || (s->in_ch != 16 && s->in_ch != 36) || s->out_ch != 16) return WAN_E_SHAPE;
   if (s->frames < 1 || s->height < 2 || s->width < 2 || (s->height & 1) || (s->width & 1)) return WAN_E_SHAPE;
   if (s->dim < 256 || s->dim % 256 != 0 || s->dim > MAX_DIM) return WAN_E_SHAPE;
   if (s->heads < 1 || s->dim % s->heads != 0) return WAN_E_SHAPE;
   const int hd = s->dim / s->heads;
   if (hd != 64 && hd != 128) return WAN_E_SHAPE;
-  if (s->mode == WAN_BF16_QK8 && hd != 128) return WAN_E_SHAPE;
+  if ((s->mode == WAN_BF16_QK8 || s->mode == WAN_FP8) && hd != 128) return WAN_E_SHAPE;
   if (s->ffn_dim < 256 || s->ffn_dim % 256 != 0 || s->ffn_dim > (1 << 16)) return WAN_E_SHAPE;
   if (s->txt_len < 1 || s->img_len < 0 || s->txt_len + s->img_len > MAX_CTX) return WAN_E_SHAPE;
   const long long L = (long long)s->frames * (s->height / 2) * (s->width / 2);
@@ -67,7 +68,8 @@ int check_shape(const wan_shape* s, Dims* d) {
     d->Ltp = pad64(s->txt_len);
     d->Lip = pad64(s->img_len);
     d->mode = s->mode == WAN_FP32 ? WAN_FP32 : WAN_BF16;  // element type of the operands
-    d->qk8 = s->mode == WAN_BF16_QK8;
+    d->qk8 = s->mode == WAN_BF16_QK8 || s->mode == WAN_FP8;
+    d->fp8 = s->mode == WAN_FP8;
     d->es = d->mode == WAN_BF16 ? 2 : 4;
   }
   return WAN_OK;
@@ -75,8 +77,34 @@ int check_shape(const wan_shape* s, Dims* d) {
 
 // Offsets (bytes) inside the workspace of one block run over Bb batch rows.
 struct BlockPlan {
-  size_t m, r1, q, k, vt, o, ck, cvt, ik, ivt, rope, ropet, total;
+  size_t m, r1, q, k, vt, o, ck, cvt, ik, ivt, rope, ropet;
+  // WAN_FP8: e4m3 LayerNorm outputs and their scales, e4m3 FFN hidden and its
+  // scales, the block's e4m3 projection weights and their scales
+  size_t m8, msc, h8, hsc, w8, wsc;
+  size_t total;
 };
+
+// offsets of the four 8-bit weight matrices inside BlockPlan::w8 / ::wsc
+struct W8Plan {
+  size_t qkv, cq, ff1, ff2;       // bytes into w8
+  size_t sqkv, scq, sff1, sff2;   // bytes into wsc
+  size_t w_bytes, s_bytes;
+};
+W8Plan plan_w8(const Dims& d) {
+  W8Plan w;
+  const size_t D = d.D, F = d.Ff;
+  w.qkv = 0;
+  w.cq = 3 * D * D;
+  w.ff1 = 4 * D * D;
+  w.ff2 = 4 * D * D + F * D;
+  w.w_bytes = 4 * D * D + 2 * F * D;
+  w.sqkv = 0;
+  w.scq = (D / 128) * 3 * D;
+  w.sff1 = (D / 128) * 4 * D;
+  w.sff2 = (D / 128) * (4 * D + F);
+  w.s_bytes = (D / 128) * (4 * D + F) + (F / 128) * D;
+  return w;
+}
 
 size_t rope_entries(const Dims& d) {
   const int ds = 2 * (d.hd / 6), df = d.hd - 2 * ds;
@@ -113,6 +141,23 @@ BlockPlan plan_block(const Dims& d, int Bb, size_t base) {
   off += al(rope_entries(d) * sizeof(float2));
   p.ropet = off;
   off += al((size_t)d.L * (d.hd / 2) * sizeof(float2));
+  p.m8 = p.msc = p.h8 = p.hsc = p.w8 = p.wsc = off;
+  if (d.fp8) {
+    const size_t rows_p = (size_t)Bb * pad256(d.L);  // padded token rows of the 8-bit GEMMs
+    const W8Plan w8 = plan_w8(d);
+    p.m8 = off;
+    off += al((size_t)Bb * d.L * d.D);
+    p.msc = off;
+    off += al((size_t)(d.D / 128) * rows_p);
+    p.h8 = off;
+    off += al(rows_p * d.Ff);
+    p.hsc = off;
+    off += al((size_t)(d.Ff / 128) * rows_p);
+    p.w8 = off;
+    off += al(w8.w_bytes);
+    p.wsc = off;
+    off += al(w8.s_bytes);
+  }
   p.total = off;
   return p;
 }
@@ -284,11 +329,43 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     HIP_TRY(launch_rope_tokens(ropet, rope, d.hd, d.F, d.Hh, d.Ww, st));
   }
 
+  // WAN_FP8: the 8-bit projections take e4m3 operands with scales per 128-block;
+  // the weights are quantised here, the activations by the kernels producing them
+  unsigned char* m8 = reinterpret_cast<unsigned char*>(at(ws, p.m8));
+  unsigned char* msc = reinterpret_cast<unsigned char*>(at(ws, p.msc));
+  const long long rows_p = (long long)Bb * P;
+  const W8Plan w8p = plan_w8(d);
+  unsigned char* w8 = reinterpret_cast<unsigned char*>(at(ws, p.w8));
+  unsigned char* wsc = reinterpret_cast<unsigned char*>(at(ws, p.wsc));
+  if (d.fp8) {
+    if (attn_mode != ATTN_REUSE)
+      HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_quant_weights(w->qkv_w, w8 + w8p.qkv, wsc + w8p.sqkv, 3 * d.D, d.D, st); }));
+    HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_quant_weights(w->cq_w, w8 + w8p.cq, wsc + w8p.scq, d.D, d.D, st); }));
+    HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_quant_weights(w->ff1_w, w8 + w8p.ff1, wsc + w8p.sff1, d.Ff, d.D, st); }));
+    HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_quant_weights(w->ff2_w, w8 + w8p.ff2, wsc + w8p.sff2, d.D, d.Ff, st); }));
+  }
+  // LayerNorm (+ modulation) of x into m, or into m8 / msc for an 8-bit projection
+  auto ln = [&](const float* shift, const float* scale) {
+    if (d.fp8)
+      return timed(WAN_KERNEL_ELEMENTWISE, st, [&] {
+        return launch_ln_mod8(x, m8, msc, rows_p, P, M, d.D, d.L, shift, scale, shift ? mbs : 0, st);
+      });
+    return timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, shift, scale, shift ? mbs : 0, st); });
+  };
+  // A operand of a projection whose input is the LayerNorm output
+  auto ln_operand = [&](GemmArgs& g, size_t w8_off, size_t ws_off) {
+    if (d.fp8) {
+      g.A = m8; g.a_scale = msc; g.a_sld = rows_p;
+      g.Wt = w8 + w8_off; g.w_scale = wsc + ws_off;
+    }
+  };
+  const int ld_loader = d.fp8 ? LOAD_FP8 : LOAD_PLAIN;
+
   // self-attention sublayer (its attention output optionally written to, or
   // taken from, the diffusion cache)
   T* a_out = attn_mode == ATTN_COMPUTE ? o : reinterpret_cast<T*>(attn_io);
   if (attn_mode != ATTN_REUSE) {
-  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, mod + 0 * d.D, mod + 1 * d.D, mbs, st); }));
+  HIP_TRY(ln(mod + 0 * d.D, mod + 1 * d.D));
   HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.vt), Bb * d.heads, d.hd, d.L, d.Lp, st));
   {
     GemmArgs g;
@@ -304,7 +381,8 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
       g.qs = reinterpret_cast<unsigned char*>(at(ws, p.q + qk8_bytes(d, Bb)));
       g.ks = reinterpret_cast<unsigned char*>(at(ws, p.k + qk8_bytes(d, Bb)));
     }
-    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, d.qk8 ? EPI_PACK8 : EPI_PACK, st); }));
+    ln_operand(g, w8p.qkv, w8p.sqkv);
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, ld_loader, d.qk8 ? EPI_PACK8 : EPI_PACK, st); }));
   }
   {
     AttnArgs a;
@@ -329,7 +407,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
   }
 
   // cross-attention sublayer (ungated)
-  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, nullptr, nullptr, 0, st); }));
+  HIP_TRY(ln(nullptr, nullptr));
   {
     GemmArgs g;
     g.M = Bb * P; g.N = d.D; g.K = d.D;
@@ -337,7 +415,8 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     g.Wt = w->cq_w; g.ldw = d.D; g.bias = w->cq_b;
     g.c_rpb = P; g.c_valid = d.L; g.q = at(ws, p.q); g.nq = d.D; g.nk = 0;
     g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
-    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_PACK, st); }));
+    ln_operand(g, w8p.cq, w8p.scq);
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, ld_loader, EPI_PACK, st); }));
   }
   {
     GemmArgs g;
@@ -383,7 +462,30 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
   }
 
   // FFN sublayer
-  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, mod + 3 * d.D, mod + 4 * d.D, mbs, st); }));
+  HIP_TRY(ln(mod + 3 * d.D, mod + 4 * d.D));
+  if (d.fp8) {
+    // FFN1 + GELU writes e4m3 rows (padded pitch) with scales per 128 columns; FFN2 reads them
+    unsigned char* h8 = reinterpret_cast<unsigned char*>(at(ws, p.h8));
+    unsigned char* hsc = reinterpret_cast<unsigned char*>(at(ws, p.hsc));
+    {
+      GemmArgs g;
+      g.M = (int)rows_p; g.N = d.Ff; g.K = d.D;
+      g.lda = d.D; g.a_rpb = P; g.a_bstride = (long long)d.L * d.D; g.a_valid = d.L;
+      g.ldw = d.D; g.bias = w->ff1_b;
+      ln_operand(g, w8p.ff1, w8p.sff1);
+      g.c_rpb = P; g.C = h8; g.ldc = d.Ff; g.c_scale = hsc; g.c_sld = rows_p;
+      HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_FP8, EPI_STORE_GELU8, st); }));
+    }
+    {
+      GemmArgs g;
+      g.M = (int)rows_p; g.N = d.D; g.K = d.Ff;
+      g.A = h8; g.lda = d.Ff; g.a_rpb = (int)rows_p; g.a_scale = hsc; g.a_sld = rows_p;
+      g.Wt = w8 + w8p.ff2; g.w_scale = wsc + w8p.sff2; g.ldw = d.Ff; g.bias = w->ff2_b;
+      g.c_rpb = P; g.c_valid = d.L; g.x = x; g.ldx = d.D; g.gate = mod + 5 * d.D; g.gate_bstride = mbs;
+      HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_FP8, EPI_RESID, st); }));
+    }
+    return WAN_OK;
+  }
   T* hbuf = reinterpret_cast<T*>(at(ws, p.r1));
   {
     GemmArgs g;

@@ -84,6 +84,25 @@ __device__ __forceinline__ void pack8(Chunk<float>& c, const float* f) {
   c.b = (f32x4){f[4], f[5], f[6], f[7]};
 }
 
+// 8-bit operands: e4m3 values (bias 7, largest finite 448) with one power-of-two
+// scale 2^e per block, kept as the byte e + 127.  e is the smallest exponent with
+// max|block| / 2^e <= 448, clamped to [-127, 127], and 0 for an all-zero block:
+// with max|block| = m 2^E, m in [1, 2), that is E - 8, plus one when m > 1.75.
+__device__ __forceinline__ int e8_exponent(float amax) {
+  const unsigned ab = __float_as_uint(amax);
+  const int ef = (int)(ab >> 23);
+  const int ex = ef == 0 ? (amax == 0.f ? 0 : -127) : ef - 135 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return ex < -127 ? -127 : ex;
+}
+// 8 values times inv (= 2^-e, an exact scaling) rounded to e4m3, nearest-even, 8 bytes
+__device__ __forceinline__ uint2 e4m3_pack8(const float* v, float inv) {
+  unsigned w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * inv, v[1] * inv, 0u, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * inv, v[3] * inv, w0, true);
+  unsigned w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * inv, v[5] * inv, 0u, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * inv, v[7] * inv, w1, true);
+  return make_uint2(w0, w1);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -16,10 +16,38 @@ constexpr int LN_MAX_V4 = 20;  // up to D = 5120 per wave (20 float4 per lane)
 // next row's loads in flight while the current one is reduced, and keeps the
 // modulation vectors of its batch item in registers instead of re-reading them
 // for every row.
-template <typename T, int NV>
+// 8-bit output of the LayerNorm kernels: e4m3 bytes [rows][D] and one scale byte per
+// (row, 128-column block) at sc[(col / 128) * sc_ld + b * pitch + t] for row = b * rows_per_batch + t
+struct LnQ8 {
+  unsigned char* out = nullptr;
+  unsigned char* sc = nullptr;
+  long long sc_ld = 0;
+  int pitch = 0;
+};
+
+// the four values of a lane at column col (a 128-column block is 32 lanes: half a wave)
+__device__ __forceinline__ void ln_store_q8(const LnQ8& q8, const float (&r)[4], int row, int col, int lane, int D,
+                                            int rows_per_batch) {
+  float am = __builtin_elementwise_maximum(__builtin_elementwise_maximum(fabsf(r[0]), fabsf(r[1])),
+                                           __builtin_elementwise_maximum(fabsf(r[2]), fabsf(r[3])));
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) am = __builtin_elementwise_maximum(am, __shfl_xor(am, o, 64));
+  const int ex = e8_exponent(am);
+  const float inv = __uint_as_float((unsigned)(127 - ex) << 23);
+  unsigned w = __builtin_amdgcn_cvt_pk_fp8_f32(r[0] * inv, r[1] * inv, 0u, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(r[2] * inv, r[3] * inv, w, true);
+  *reinterpret_cast<unsigned*>(q8.out + (long long)row * D + col) = w;
+  if ((lane & 31) == 0) {
+    const int b = row / rows_per_batch, t = row - b * rows_per_batch;
+    q8.sc[(long long)(col >> 7) * q8.sc_ld + (long long)b * q8.pitch + t] = (unsigned char)(ex + 127);
+  }
+}
+
+template <typename T, int NV, bool Q8 = false>
 __global__ __launch_bounds__(256) void ln_mod_rows_kernel(const float* __restrict__ x, T* __restrict__ out, int rows,
                                                           int R, int rows_per_batch, const float* __restrict__ shift,
-                                                          const float* __restrict__ scale, long long mod_bstride) {
+                                                          const float* __restrict__ scale, long long mod_bstride,
+                                                          LnQ8 q8 = LnQ8()) {
   constexpr int D = NV * 256;
   const int lane = threadIdx.x & 63;
   const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
@@ -70,7 +98,9 @@ __global__ __launch_bounds__(256) void ln_mod_rows_kernel(const float* __restric
         r[2] = r[2] * (1.f + sc4[i].z) + sh4[i].z;
         r[3] = r[3] * (1.f + sc4[i].w) + sh4[i].w;
       }
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (Q8) {
+        ln_store_q8(q8, r, row, col, lane, D, rows_per_batch);
+      } else if constexpr (sizeof(T) == 2) {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 o4;
 #pragma unroll
@@ -85,10 +115,11 @@ __global__ __launch_bounds__(256) void ln_mod_rows_kernel(const float* __restric
   }
 }
 
-template <typename T>
+template <typename T, bool Q8 = false>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, T* __restrict__ out, int rows,
                                                      int D, int rows_per_batch, const float* __restrict__ shift,
-                                                     const float* __restrict__ scale, long long mod_bstride) {
+                                                     const float* __restrict__ scale, long long mod_bstride,
+                                                     LnQ8 q8 = LnQ8()) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -132,7 +163,9 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
         r[2] = r[2] * (1.f + s4.z) + h4.z;
         r[3] = r[3] * (1.f + s4.w) + h4.w;
       }
-      if (sizeof(T) == 2) {
+      if constexpr (Q8) {
+        ln_store_q8(q8, r, row, col, lane, D, rows_per_batch);
+      } else if (sizeof(T) == 2) {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 o4;
         o4[0] = to_bf16(r[0]);
@@ -274,7 +307,64 @@ __global__ void unpatch_kernel(const float* __restrict__ p, const float* __restr
   }
 }
 
+// W [N][K] bf16 -> e4m3 bytes [N][K] plus one scale byte per (row, 128-block) at
+// sc[blk * N + n]; one wave per block, two elements per lane
+__global__ __launch_bounds__(256) void quant_w_kernel(const bf16* __restrict__ W, unsigned char* __restrict__ W8,
+                                                      unsigned char* __restrict__ sc, int N, int K) {
+  const int nkb = K >> 7;
+  const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= (long long)N * nkb) return;
+  const int lane = threadIdx.x & 63;
+  const int n = (int)(wid / nkb), kb = (int)(wid - (long long)n * nkb);
+  const long long off = (long long)n * K + kb * 128 + 2 * lane;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p = *reinterpret_cast<const bf16x2*>(W + off);
+  const float a = (float)p[0], b = (float)p[1];
+  float am = __builtin_elementwise_maximum(fabsf(a), fabsf(b));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) am = __builtin_elementwise_maximum(am, __shfl_xor(am, o, 64));
+  const int ex = e8_exponent(am);
+  const float inv = __uint_as_float((unsigned)(127 - ex) << 23);
+  const unsigned w = __builtin_amdgcn_cvt_pk_fp8_f32(a * inv, b * inv, 0u, false);
+  *reinterpret_cast<unsigned short*>(W8 + off) = (unsigned short)(w & 0xFFFFu);
+  if (lane == 0) sc[(long long)kb * N + n] = (unsigned char)(ex + 127);
+}
+
 }  // namespace
+
+hipError_t launch_quant_weights(const void* W, unsigned char* W8, unsigned char* sc, int N, int K, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  if (K % 128 != 0) return hipErrorInvalidValue;
+  const long long waves = (long long)N * (K / 128);
+  hipLaunchKernelGGL(quant_w_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                     reinterpret_cast<const bf16*>(W), W8, sc, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_mod8(const float* x, unsigned char* out8, unsigned char* sc, long long sc_ld, int pitch, int rows,
+                          int D, int rows_per_batch, const float* shift, const float* scale, long long mod_bstride,
+                          hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (D % 256 != 0 || D / 256 > LN_MAX_V4 || pitch < rows_per_batch) return hipErrorInvalidValue;
+  if ((shift == nullptr) != (scale == nullptr)) return hipErrorInvalidValue;
+  LnQ8 q8;
+  q8.out = out8;
+  q8.sc = sc;
+  q8.sc_ld = sc_ld;
+  q8.pitch = pitch;
+  constexpr int R = 8;
+  const dim3 grid_r((rows + 4 * R - 1) / (4 * R));
+  bf16* o = nullptr;
+  switch (D / 256) {
+    case 1: hipLaunchKernelGGL((ln_mod_rows_kernel<bf16, 1, true>), grid_r, dim3(256), 0, st, x, o, rows, R, rows_per_batch, shift, scale, mod_bstride, q8); break;
+    case 2: hipLaunchKernelGGL((ln_mod_rows_kernel<bf16, 2, true>), grid_r, dim3(256), 0, st, x, o, rows, R, rows_per_batch, shift, scale, mod_bstride, q8); break;
+    case 6: hipLaunchKernelGGL((ln_mod_rows_kernel<bf16, 6, true>), grid_r, dim3(256), 0, st, x, o, rows, R, rows_per_batch, shift, scale, mod_bstride, q8); break;
+    default:
+      hipLaunchKernelGGL((ln_mod_kernel<bf16, true>), dim3((rows + 3) / 4), dim3(256), 0, st, x, o, rows, D,
+                         rows_per_batch, shift, scale, mod_bstride, q8);
+  }
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_ln_mod(const float* x, void* out, int rows, int D, int rows_per_batch, const float* shift,

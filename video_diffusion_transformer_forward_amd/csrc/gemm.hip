@@ -22,15 +22,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <typename T, int BM, int BN, int WM, int WN, int NST_, int RB, int LOADER, int EPI>
 struct Gemm {
-  static constexpr int BK = RB / (int)sizeof(T);       // k-tile depth
-  static constexpr int CPR = BK / 8;                   // chunks per tile row
+  static constexpr bool F8 = LOADER == LOAD_FP8;       // e4m3 operands (T: output type)
+  static constexpr int BK = F8 ? RB : RB / (int)sizeof(T);  // k-tile depth
+  static constexpr int CPR = F8 ? RB / 16 : BK / 8;    // chunks per tile row (16-byte chunks for e4m3)
   static constexpr int PPR = RB / 16;                  // 16-byte pieces per tile row
   static constexpr int RPD = 64 / PPR;                 // tile rows per LDS-DMA wave instruction
   static constexpr int NST = NST_;                     // LDS ring stages
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
   static constexpr int STAGE = (BM + BN) * CPR;  // chunks per stage
-  static constexpr size_t PIPE_BYTES = (size_t)NST * STAGE * sizeof(Chunk<T>);
+  // e4m3: per stage, the scale bytes of the tile's A and W rows (64 rows per wave, 256-byte slots)
+  static constexpr int SC_STAGE = F8 ? 256 * WM * WN : 0;
+  static constexpr size_t DATA_BYTES = (size_t)NST * STAGE * sizeof(Chunk<T>);
+  static constexpr size_t PIPE_BYTES = DATA_BYTES + (size_t)NST * SC_STAGE;
   // DMA instructions per wave per k-tile: each covers RPD rows
   static constexpr int NW = WM * WN;                   // waves per workgroup
   static constexpr int NT = 64 * NW;                   // threads per workgroup
@@ -55,6 +59,8 @@ struct Gemm {
   static_assert(NA * RPD * NW == BM && NB * RPD * NW == BN, "DMA split");
   static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
+  static_assert(!F8 || (BM == 256 && BN == 256 && WM * WN == 8 && RB == 64 && sizeof(T) == 2),
+                "e4m3 operands: 256x256 tiles of 8 waves, 64-byte k-tiles, bf16 output");
 };
 
 // Physical chunk position of logical chunk c in tile row r (RB-byte rows).  A
@@ -195,7 +201,101 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       for (int j = 0; j < TN; ++j) mma32(acc[i][j], fb[buf][j], fa[buf][i]);
   };
 
-  if constexpr (LOADER == LOAD_PLAIN) {
+  if constexpr (LOADER == LOAD_FP8) {
+    // ---- e4m3 operands: the LDS-DMA ring of the bf16 path with 64-byte k-tiles
+    // (64 elements, one scaled 32x32x64 MFMA step) plus, per stage, the scale
+    // bytes of the tile's 256 A rows (waves 0-3) and 256 W rows (waves 4-7) for
+    // the k-tile's 128-block.  MFMA row operand = W rows (scale_a), column operand
+    // = A rows (scale_b), as in the bf16 path.
+    constexpr int NA = C::NA, NB = C::NB, DPT = NA + NB + 1, RPD = C::RPD, PPR = C::PPR;
+    const int pp = lane % PPR;
+    const int rlow = lane / PPR;
+    const unsigned char* a_src[NA];
+    const unsigned char* b_src[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int rt = (wave * NA + i) * RPD + rlow;
+      const int r = min(m0 + rt, g.M - 1);
+      const int bb = r / g.a_rpb;
+      int t = r - bb * g.a_rpb;
+      if (g.a_valid > 0) t = min(t, g.a_valid - 1);
+      a_src[i] = reinterpret_cast<const unsigned char*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda +
+                 swz<RB, CPR>(rt, pp) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int rt = (wave * NB + i) * RPD + rlow;
+      b_src[i] = reinterpret_cast<const unsigned char*>(g.Wt) + (long long)(n0 + rt) * g.ldw + swz<RB, CPR>(rt, pp) * 16;
+    }
+    // scale rows: a 64-byte run per wave, lanes past 15 repeat the last word into the slot's tail
+    const bool sc_a = wave < 4;
+    const unsigned char* sc_src = (sc_a ? g.a_scale + m0 + 64 * wave : g.w_scale + n0 + 64 * (wave - 4)) +
+                                  4 * (lane < 16 ? lane : 15);
+    const long long sc_ld = sc_a ? g.a_sld : (long long)g.N;
+    auto issue = [&](int kt) {
+      const int st = kt % NST;
+      unsigned char* base = smem_raw + (size_t)st * C::STAGE * sizeof(Chunk<T>);
+      const int koff = kt * BK;
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        __builtin_amdgcn_global_load_lds(a_src[i] + koff, (lds_void*)(base + (size_t)(wave * NA + i) * 1024), 16,
+                                         0, 0);
+      unsigned char* bbase = base + (size_t)BM * RB;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        __builtin_amdgcn_global_load_lds(b_src[i] + koff, (lds_void*)(bbase + (size_t)(wave * NB + i) * 1024), 16,
+                                         0, 0);
+      __builtin_amdgcn_global_load_lds(sc_src + (long long)(koff / 128) * sc_ld,
+                                       (lds_void*)(smem_raw + C::DATA_BYTES + (size_t)st * C::SC_STAGE + wave * 256),
+                                       4, 0, 0);
+    };
+    constexpr int INFLIGHT = (NST - 2) * DPT;
+    auto issue_c = [&](int kt) { issue(min(kt, nk - 1)); };
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    i32x8 fa[TM], fb[TN];
+    int sa8[TM], sb8[TN];
+    auto load_frags8 = [&](int st) {
+      const unsigned char* sa = smem_raw + (size_t)st * C::STAGE * sizeof(Chunk<T>);
+      const unsigned char* sb = sa + (size_t)BM * RB;
+      const unsigned char* sc = smem_raw + C::DATA_BYTES + (size_t)st * C::SC_STAGE;
+      auto rd32 = [&](const unsigned char* rowp, int r) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + swz<RB, CPR>(r, 2 * g2) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(rowp + swz<RB, CPR>(r, 2 * g2 + 1) * 16);
+        return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = brow0 + 32 * j + l32;
+        fb[j] = rd32(sb + r * RB, r);
+        sb8[j] = sc[(4 + r / 64) * 256 + r % 64];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = arow0 + 32 * i + l32;
+        fa[i] = rd32(sa + r * RB, r);
+        sa8[i] = sc[(r / 64) * 256 + r % 64];
+      }
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < NST - 1; ++s0) issue_c(s0);
+    wait_vmcnt<INFLIGHT>();
+    barrier_lds();
+    load_frags8(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      issue_c(kt + NST - 1);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sb8[j], 0,
+                                                                      sa8[i]);
+      wait_vmcnt<INFLIGHT>();  // k-tile kt+1 (and its scales) have landed
+      barrier_lds();
+      load_frags8((kt + 1) % NST);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  } else if constexpr (LOADER == LOAD_PLAIN) {
     // ---- LDS-DMA ring.  One wave instruction fills 1 KB = RPD tile rows; lane
     // l writes the l-th 16 bytes, so the chunk swizzle is applied to the global
     // address each lane reads.
@@ -499,7 +599,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             v[4 + u] += b1[u];
           }
         }
-        if (EPI == EPI_STORE || EPI == EPI_STORE_GELU) {
+        if constexpr (EPI == EPI_STORE_GELU8) {
+          // GELU, then e4m3 with one power-of-two scale per (row, 128-column block):
+          // the 16 lanes of this row within the 128-column slab hold the block
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = gelu_erf(v[u]);
+          float am = 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) am = __builtin_elementwise_maximum(am, fabsf(v[u]));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) am = __builtin_elementwise_maximum(am, __shfl_xor(am, o, 64));
+          const int ex = e8_exponent(am);
+          const float inv = __uint_as_float((unsigned)(127 - ex) << 23);
+          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(g.C) + (long long)row * g.ldc + n) =
+              e4m3_pack8(v, inv);
+          if ((n & 127) == 0) g.c_scale[(long long)(n >> 7) * g.c_sld + row] = (unsigned char)(ex + 127);
+        } else if (EPI == EPI_STORE || EPI == EPI_STORE_GELU) {
           if (EPI == EPI_STORE_GELU) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = gelu_erf(v[u]);
@@ -512,7 +627,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           pack8(c, v);
           c.store(reinterpret_cast<float*>(g.C) + (long long)row * g.ldc + n);
         } else if (EPI == EPI_RESID) {
-          float* xp = g.x + (long long)row * g.ldx + n;
+          long long xrow = row;
+          if (g.c_valid > 0) {
+            // padded row pitch: token t of batch item b is residual row b * c_valid + t
+            const int b = row / g.c_rpb, t = row - b * g.c_rpb;
+            if (t >= g.c_valid) continue;
+            xrow = (long long)b * g.c_valid + t;
+          }
+          float* xp = g.x + xrow * g.ldx + n;
           f32x4 x0 = *reinterpret_cast<const f32x4*>(xp);
           f32x4 x1 = *reinterpret_cast<const f32x4*>(xp + 4);
           if (g.gate) {
@@ -554,26 +676,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
           const long long rowidx = ((long long)b * g.heads + hh) * g.Lp + t;
           if constexpr (EPI == EPI_PACK8) {
-            // e4m3 with one power-of-two scale per (token, head): 2^e with the
-            // smallest e (clamped to [-127, 127]) that brings max|row| to 448 or
-            // below, stored as the E8M0 byte e + 127.  max|row| gathers over the
-            // 16 lanes of the head; frexp(amax) = m 2^E gives e = E - 9 + (m > 7/8).
+            // e4m3 with one power-of-two scale per (token, head), stored as the
+            // byte e + 127 (e8_exponent); max|row| gathers over the 16 lanes of the head
             float am = 0.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) am = __builtin_elementwise_maximum(am, fabsf(v[u]));
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) am = __builtin_elementwise_maximum(am, __shfl_xor(am, o, 64));
-            const unsigned ab = __float_as_uint(am);
-            const int ef = (int)(ab >> 23);
-            int ex = ef == 0 ? (am == 0.f ? 0 : -127) : ef - 135 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-            ex = ex < -127 ? -127 : ex;
+            const int ex = e8_exponent(am);
             const float inv = __uint_as_float((unsigned)(127 - ex) << 23);  // 2^-e, exact scaling
-            unsigned w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * inv, v[1] * inv, 0u, false);
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * inv, v[3] * inv, w0, true);
-            unsigned w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * inv, v[5] * inv, 0u, false);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * inv, v[7] * inv, w1, true);
             unsigned char* base = reinterpret_cast<unsigned char*>(sec == 0 ? g.q : g.k);
-            *reinterpret_cast<uint2*>(base + rowidx * g.hd + e0) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(base + rowidx * g.hd + e0) = e4m3_pack8(v, inv);
             if (e0 == 0) (sec == 0 ? g.qs : g.ks)[rowidx] = (unsigned char)(ex + 127);
           } else {
             Chunk<T> c;
@@ -600,7 +713,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   using C = Gemm<T, BM, BN, WM, WN, NST, RB, LOADER, EPI>;
   static_assert(OCC * C::LDS_BYTES <= 160 * 1024, "occupancy exceeds the LDS");
   if (g.N % BN != 0) return hipErrorInvalidValue;
-  if (LOADER == LOAD_PLAIN && g.K % C::BK != 0) return hipErrorInvalidValue;
+  if ((LOADER == LOAD_PLAIN || LOADER == LOAD_FP8) && g.K % C::BK != 0) return hipErrorInvalidValue;
   auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, RB, OCC, LOADER, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -642,9 +755,30 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
   if (g.M <= 0) return hipSuccess;
   // the LDS-DMA path streams whole k-tiles: K must be a multiple of the k-tile depth
   constexpr int BK = sizeof(T) == 2 ? 32 : 16;
+  if (loader == LOAD_FP8 && epi != EPI_PACK && epi != EPI_PACK8 && epi != EPI_STORE_GELU8 && epi != EPI_RESID)
+    return hipErrorInvalidValue;
   if (loader == LOAD_PLAIN && g.K % BK != 0) return hipErrorInvalidValue;
   if (loader == LOAD_PATCH) {
     if (epi == EPI_STORE_F32) return launch_by_n<T, LOAD_PATCH, EPI_STORE_F32>(g, st);
+    return hipErrorInvalidValue;
+  }
+  if (loader == LOAD_FP8) {
+    // e4m3 operands: 256x256 tiles of 8 waves; M a whole number of tiles (the scale
+    // rows of a tile are read as one 256-byte run), K whole 128-blocks
+    if constexpr (sizeof(T) == 2) {
+      if (g.N % 256 != 0 || g.K % 128 != 0 || g.M % 256 != 0 || !g.a_scale || !g.w_scale || g.a_sld < g.M)
+        return hipErrorInvalidValue;
+      switch (epi) {
+        case EPI_PACK: return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_PACK>(g, st);
+        case EPI_PACK8:
+          if (g.hd != 128 || !g.qs || !g.ks) return hipErrorInvalidValue;
+          return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_PACK8>(g, st);
+        case EPI_STORE_GELU8:
+          if (!g.c_scale || g.c_sld < g.M) return hipErrorInvalidValue;
+          return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_STORE_GELU8>(g, st);
+        case EPI_RESID: return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_RESID>(g, st);
+      }
+    }
     return hipErrorInvalidValue;
   }
   switch (epi) {

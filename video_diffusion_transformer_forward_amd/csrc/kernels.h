@@ -6,8 +6,14 @@
 
 namespace wan {
 
-enum Loader { LOAD_PLAIN = 0, LOAD_PATCH = 1 };
-enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_STORE_F32 = 2, EPI_RESID = 3, EPI_PACK = 4, EPI_PACK8 = 5 };
+// LOAD_FP8 (T = bf16 output type): A and W are e4m3 bytes with one power-of-two
+// scale byte (exponent + 127) per 128-element block along K: A scales at
+// a_scale[blk * a_sld + r] for GEMM row r, W scales at w_scale[blk * N + n]
+enum Loader { LOAD_PLAIN = 0, LOAD_PATCH = 1, LOAD_FP8 = 2 };
+// EPI_STORE_GELU8: GELU, then e4m3 bytes at C + r * ldc + n with one scale byte per
+// (row, 128-column block) at c_scale[(n / 128) * c_sld + r]
+enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_STORE_F32 = 2, EPI_RESID = 3, EPI_PACK = 4, EPI_PACK8 = 5,
+           EPI_STORE_GELU8 = 6 };
 
 // C[M][N] = A[M][K] * W[N][K]^T + bias, with an epilogue selected by `epi`.
 struct GemmArgs {
@@ -18,6 +24,10 @@ struct GemmArgs {
   long long lda = 0, a_bstride = 0;
   int a_rpb = 1;
   int a_valid = 0;
+  // LOAD_FP8 scale bytes (blocks of 128 along K)
+  const unsigned char* a_scale = nullptr;
+  long long a_sld = 0;
+  const unsigned char* w_scale = nullptr;
   // A operand (LOAD_PATCH): (1,2,2) patches of [z ; cond], token rows of `zb_count` videos
   const float* z = nullptr;
   const float* cond = nullptr;
@@ -28,13 +38,16 @@ struct GemmArgs {
   long long ldw = 0;
   const float* bias = nullptr;
   // rows of C belong to batch b = r / c_rpb, token t = r % c_rpb; with c_valid > 0
-  // (EPI_PACK only) tokens t >= c_valid are padding and not stored
+  // (EPI_PACK*, EPI_RESID) tokens t >= c_valid are padding and not stored
   int c_rpb = 1;
   int c_valid = 0;
   // EPI_STORE*: C + r * ldc + n
   void* C = nullptr;
   long long ldc = 0;
-  // EPI_RESID: x[r * ldx + n] += gate[b * gate_bstride + n] * (acc + bias); gate NULL -> 1
+  unsigned char* c_scale = nullptr;  // EPI_STORE_GELU8
+  long long c_sld = 0;
+  // EPI_RESID: x[xr * ldx + n] += gate[b * gate_bstride + n] * (acc + bias); gate NULL -> 1;
+  // xr = r, or b * c_valid + t when c_valid > 0
   float* x = nullptr;
   long long ldx = 0;
   const float* gate = nullptr;
@@ -80,6 +93,15 @@ template <typename T> hipError_t launch_attention(const AttnArgs& a, hipStream_t
 template <typename T>
 hipError_t launch_ln_mod(const float* x, void* out, int rows, int D, int rows_per_batch, const float* shift,
                          const float* scale, long long mod_bstride, hipStream_t st);
+
+// As launch_ln_mod, with e4m3 output bytes out8 [rows][D] and one scale byte per
+// (row, 128-column block) at sc[(col / 128) * sc_ld + b * pitch + t], row = b * rows_per_batch + t
+hipError_t launch_ln_mod8(const float* x, unsigned char* out8, unsigned char* sc, long long sc_ld, int pitch, int rows,
+                          int D, int rows_per_batch, const float* shift, const float* scale, long long mod_bstride,
+                          hipStream_t st);
+
+// bf16 weights W [N][K] -> e4m3 bytes W8 [N][K] and scale bytes sc [K/128][N] (blocks of 128 along K)
+hipError_t launch_quant_weights(const void* W, unsigned char* W8, unsigned char* sc, int N, int K, hipStream_t st);
 
 // (cos, sin) RoPE table for head dim hd over grid (F, Hh, Ww), computed in double: the
 // frame segment, then the row and column segments, one entry per (position, pair).

@@ -40,6 +40,7 @@ class WanConfig:
     n_blocks: int = 1
     mode: str = "fp32"       # "fp32" or "bf16"
     qk8: bool = False        # bf16 only: self-attention scores from 8-bit q and k
+    fp8: bool = False        # bf16 only: 8-bit projections (q/k/v, cross q, FFN) plus qk8
     timestep: float = 500.0
     dt: float = 0.05
     guide_scale: float = 5.0
