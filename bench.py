@@ -150,7 +150,7 @@ def main():
     ap.add_argument("--config", default="wan13b_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-modes", action="store_true", help="skip timing the diffusion-cache step modes")
-    ap.add_argument("--no-qk8", action="store_true", help="skip timing the step with 8-bit self-attention scores")
+    ap.add_argument("--no-qk8", action="store_true", help="skip timing the step in the 8-bit forms")
     ap.add_argument("--block-configs", default="",
                     help="comma-separated block configurations to time one block forward of "
                          "(e.g. wan13b_block,wan14b_720p_block,wan14b_i2v_block); reported under 'blocks'")
@@ -206,26 +206,38 @@ def main():
                                            ("cross_attention", N.KERNEL_CROSS_ATTENTION),
                                            ("gemm", N.KERNEL_GEMM), ("elementwise", N.KERNEL_ELEMENTWISE))}
     assert bool(torch.isfinite(z).all())
-    # the same step with 8-bit self-attention scores (WAN_BF16_QK8; same weights)
-    qk8 = None
-    if not args.no_qk8:
-        cfg8 = cfg.with_(qk8=True)
+    # the same step in the 8-bit forms (same weights): 8-bit self-attention scores
+    # (WAN_BF16_QK8), and 8-bit projections on top (WAN_FP8)
+    def time_variant(cfg8, reps=3):
+        ws8 = W.workspace(cfg8, N.ENTRY_STEP)
         z8 = z0.clone()
-        W.denoise_step(cfg8, model, z8, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws)
+        W.denoise_step(cfg8, model, z8, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws8)
         torch.cuda.synchronize()
         W.timing_enable(True)
-        W.timing_read(N.KERNEL_SELF_ATTENTION, reset=True)
+        for k in range(4):
+            W.timing_read(k, reset=True)
         t1 = time.perf_counter()
-        for _ in range(3):
-            W.denoise_step(cfg8, model, z8, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws)
+        for _ in range(reps):
+            W.denoise_step(cfg8, model, z8, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws8)
         torch.cuda.synchronize()
-        ms8 = (time.perf_counter() - t1) / 3 * 1e3
+        ms8 = (time.perf_counter() - t1) / reps * 1e3
         W.timing_enable(False)
-        a8_ms, a8_n = W.timing_read(N.KERNEL_SELF_ATTENTION)
+        kt8 = {k: W.timing_read(c) for k, c in (("self_attention", N.KERNEL_SELF_ATTENTION),
+                                                ("cross_attention", N.KERNEL_CROSS_ATTENTION),
+                                                ("gemm", N.KERNEL_GEMM), ("elementwise", N.KERNEL_ELEMENTWISE))}
         assert bool(torch.isfinite(z8).all())
-        qk8 = {"ms_per_step": round(ms8, 3), "self_attention_ms_per_step": round(a8_ms / 3, 3),
-               "self_attention_avg_launch_ms": round(a8_ms / max(a8_n, 1), 4)}
-        del z8
+        a8_ms, a8_n = kt8["self_attention"]
+        del z8, ws8
+        torch.cuda.empty_cache()
+        return {"ms_per_step": round(ms8, 3),
+                "kernel_ms_per_step": {k: round(v[0] / reps, 3) for k, v in kt8.items()},
+                "self_attention_avg_launch_ms": round(a8_ms / max(a8_n, 1), 4)}
+
+    qk8 = fp8 = None
+    if not args.no_qk8:
+        print("[bench] 8-bit variants", file=sys.stderr, flush=True)
+        qk8 = time_variant(cfg.with_(qk8=True))
+        fp8 = time_variant(cfg.with_(fp8=True))
     # diffusion cache: one step in each mode (after a store step), timed alone
     cache_ms = None
     if not args.no_cache_modes:
@@ -298,15 +310,21 @@ def main():
                      "avg_launch_ms": round(attn_avg, 4), "launches": attn_n,
                      "flop_per_launch": bf["self_attention"]},
     }
-    if qk8 is not None:
-        a8 = qk8["self_attention_avg_launch_ms"]
-        qk8.update({
-            "tflops_equivalent": round(flops / (qk8["ms_per_step"] * 1e-3) / 1e12, 2),
-            "speedup_vs_bf16_step": round(ms_step / qk8["ms_per_step"], 4),
+    for key, var, note in (
+            ("qk8_step", qk8, "self-attention scores from e4m3 q and k (per-token power-of-two scales); P V, "
+                              "GEMMs and the rest stay bf16"),
+            ("fp8_step", fp8, "as qk8_step, plus e4m3 q/k/v, cross-attention query and FFN projections "
+                              "(power-of-two scales per 128-block of both operands, weights quantised inside the "
+                              "step); output projections, context K/V and attention P V stay bf16")):
+        if var is None:
+            continue
+        a8 = var["self_attention_avg_launch_ms"]
+        var.update({
+            "tflops_equivalent": round(flops / (var["ms_per_step"] * 1e-3) / 1e12, 2),
+            "speedup_vs_bf16_step": round(ms_step / var["ms_per_step"], 4),
             "self_attention_speedup": round(attn_avg / a8, 4) if a8 > 0 else None,
-            "note": "same step with self-attention scores from e4m3 q and k (per-token power-of-two scales); "
-                    "P V, GEMMs and the rest stay bf16; reduced-precision variant, not the headline value"})
-        out["qk8_step"] = qk8
+            "note": note + "; reduced-precision variant, not the headline value"})
+        out[key] = var
     if cache_ms is not None:
         out["diffusion_cache"] = {
             "ms_per_step": cache_ms, "cache_gb": cache_gb,
