@@ -32,11 +32,11 @@ CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 # KiB per dispatch), each scaled by known/counted bytes of the 1 GiB calibration copy in the
 # same run.  Valid only for the kernel sources they were taken on (checked by hash).
 ATTN_COUNTERS = {
-    "fetch_kib": 884902.10, "fetch_scale": 1048576 / 524307.6,
+    "fetch_kib": 884803.06, "fetch_scale": 1048576 / 524306.44,
     "write_kib": 196560.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "7be44015cdc8d05f0883a7c3f2a7188ce1177e194555c056f6f9a698ad8a4d5a",
+    "sha256": "1ea43fde7dbec62c2403aed17295014bb09172677600b523c59ee86900456be5",
 }
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 
