@@ -14,8 +14,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "wan.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(wan_[a-z_]+)\s*\(", src, re.M)))
+    names = set()
+    for h in ("wan.h", "wan_vae.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(wan_[a-z_]+)\s*\(", src, re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -195,3 +198,35 @@ def test_fp8_mode_shapes():
     sh = shape_of(get_config("toy").with_(mode="bf16", fp8=True))
     assert lib.wan_workspace_bytes(ctypes.byref(sh), N.ENTRY_BLOCK, ctypes.byref(st)) == 0
     assert st.value == N.WAN_E_SHAPE
+
+
+def test_vae_shapes_and_argument_errors():
+    """VAE decoder: parameter table against the input generator's list, workspace sizes, and
+    argument errors reported before any device work."""
+    from video_diffusion_transformer_forward_amd import vae_synth as VS
+    import video_diffusion_transformer_forward_amd as W
+    lib = N.load()
+    st = ctypes.c_int(0)
+    cfg = VS.get_vae_config("vae_w96")
+    sh = W.vae_shape_of(cfg)
+    tab = W.vae_param_table(sh)
+    assert [t[0] for t in tab if t[1] != 1] == [n for n, _ in VS.vae_param_shapes(cfg)]
+    assert all(t[3] % 64 == 0 for t in tab)
+    assert lib.wan_vae_workspace_bytes(ctypes.byref(sh), ctypes.byref(st)) > 0 and st.value == N.WAN_OK
+    assert lib.wan_vae_cache_bytes(ctypes.byref(sh), ctypes.byref(st)) > 0
+    for bad in (dict(base=48), dict(base=0), dict(z_ch=40), dict(n_res=0), dict(frames=0)):
+        b = W.vae_shape_of(cfg.with_(**bad)) if "frames" not in bad else N.WanVaeShape(0, 5, 7, 16, 96, 2, 1)
+        assert lib.wan_vae_workspace_bytes(ctypes.byref(b), ctypes.byref(st)) == 0
+        assert st.value == N.WAN_E_SHAPE
+    big = N.WanVaeShape(21, 600, 1040, 16, 96, 2, 21)
+    assert lib.wan_vae_workspace_bytes(ctypes.byref(big), ctypes.byref(st)) == 0 and st.value == N.WAN_E_SHAPE
+    F = FAKE
+    dec = lambda t0, n, ws_bytes=1 << 40, cb=1 << 40, z=F: lib.wan_vae_decode(
+        ctypes.byref(sh), F, F, z, t0, n, F, cb, F, F, ws_bytes, None)
+    assert dec(0, 5) == N.WAN_E_SHAPE          # t0 + n > frames
+    assert dec(-1, 1) == N.WAN_E_SHAPE
+    assert dec(0, 0) == N.WAN_E_SHAPE
+    assert dec(0, 1, ws_bytes=1024) == N.WAN_E_WORKSPACE
+    assert dec(0, 1, cb=16) == N.WAN_E_WORKSPACE
+    assert dec(0, 1, z=None) == N.WAN_E_NULL
+    assert dec(0, 1, z=F + 4) == N.WAN_E_ALIGN

@@ -15,7 +15,8 @@ from .synth import WanConfig
 
 __all__ = ["shape_of", "DeviceBlock", "DeviceModel", "workspace", "workspace_bytes", "patchify", "time_embed",
            "cache_bytes", "diffusion_cache", "denoise_step_cached",
-           "dit_block_forward", "head", "denoise_step", "timing_enable", "timing_read", "WanError"]
+           "dit_block_forward", "head", "denoise_step", "timing_enable", "timing_read", "WanError",
+           "vae_shape_of", "vae_param_table", "VaeDevice", "vae_workspace", "vae_cache", "vae_decode"]
 
 
 def _torch():
@@ -185,3 +186,77 @@ def denoise_step(cfg, model: DeviceModel, z, cond, ctx_cond, ctx_null, timestep,
                                  _ptr(ctx_null), float(timestep), float(dt), float(guide_scale), _ptr(ws),
                                  ws.numel(), _stream(stream)))
     return z
+
+
+# ----------------------------------------------------------------------------- Wan-VAE decoder
+def vae_shape_of(cfg, chunk=None) -> N.WanVaeShape:
+    """wan_vae_shape of a VaeConfig; chunk: most latent frames per call (default: all)."""
+    return N.WanVaeShape(cfg.frames, cfg.height, cfg.width, cfg.z_ch, cfg.base, cfg.n_res,
+                         cfg.frames if chunk is None else int(chunk))
+
+
+def vae_param_table(sh: N.WanVaeShape):
+    """[(name, kind, dims, offset, count)] from wan_vae_param_info."""
+    lib = N.load()
+    st = ctypes.c_int(0)
+    n = lib.wan_vae_param_count(ctypes.byref(sh), ctypes.byref(st))
+    N.check(st.value)
+    out = []
+    info = N.WanVaeParam()
+    for i in range(n):
+        N.check(lib.wan_vae_param_info(ctypes.byref(sh), i, ctypes.byref(info)))
+        k = info.kind
+        out.append((info.name.decode(), k, tuple(info.dims[:5 if k == 0 else 1]), int(info.offset), int(info.count)))
+    return out
+
+
+class VaeDevice:
+    """The decoder's parameters in the library's two device blobs (bf16 weights, float
+    biases and norm scales), placed by wan_vae_param_info."""
+
+    def __init__(self, sh: N.WanVaeShape, params: dict, device="cuda"):
+        import numpy as np
+        from .synth import bf16_bits
+        torch = _torch()
+        lib = N.load()
+        st = ctypes.c_int(0)
+        nw = lib.wan_vae_blob_elems(ctypes.byref(sh), 0, ctypes.byref(st))
+        N.check(st.value)
+        nf = lib.wan_vae_blob_elems(ctypes.byref(sh), 1, ctypes.byref(st))
+        N.check(st.value)
+        wb = np.zeros(max(nw, 64), np.uint16)
+        fb = np.zeros(max(nf, 64), np.float32)
+        for name, kind, dims, off, cnt in vae_param_table(sh):
+            a = np.asarray(params[name], np.float32).reshape(-1)
+            if a.size != cnt:
+                raise ValueError(f"{name}: {a.size} values, the library expects {cnt}")
+            if kind == 0:
+                wb[off:off + cnt] = bf16_bits(a)
+            else:
+                fb[off:off + cnt] = a
+        self.weights = torch.from_numpy(wb.view(np.int16)).to(device)
+        self.fparams = torch.from_numpy(fb).to(device)
+
+
+def vae_workspace(sh: N.WanVaeShape, device="cuda"):
+    torch = _torch()
+    st = ctypes.c_int(0)
+    n = N.load().wan_vae_workspace_bytes(ctypes.byref(sh), ctypes.byref(st))
+    N.check(st.value)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def vae_cache(sh: N.WanVaeShape, device="cuda"):
+    torch = _torch()
+    st = ctypes.c_int(0)
+    n = N.load().wan_vae_cache_bytes(ctypes.byref(sh), ctypes.byref(st))
+    N.check(st.value)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def vae_decode(sh: N.WanVaeShape, dev: VaeDevice, z, t0: int, n: int, cache, video, ws, stream=None):
+    """wan_vae_decode: latent frames [t0, t0 + n) of z (z_ch, n, H, W) float32 -> video
+    (3, n_out, 8H, 8W) float32."""
+    lib = N.load()
+    N.check(lib.wan_vae_decode(ctypes.byref(sh), _ptr(dev.weights), _ptr(dev.fparams), _ptr(z), int(t0), int(n),
+                               _ptr(cache), cache.numel(), _ptr(video), _ptr(ws), ws.numel(), _stream(stream)))

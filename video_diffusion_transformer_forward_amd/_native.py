@@ -1,4 +1,4 @@
-"""ctypes view of include/wan.h.  Loads the in-tree libwan.so; no fallback."""
+"""ctypes view of include/wan.h and include/wan_vae.h.  Loads the in-tree libwan.so; no fallback."""
 from __future__ import annotations
 
 import ctypes
@@ -29,7 +29,9 @@ ENTRY_HEAD = 4
 
 EXPORTS = ("wan_status_str", "wan_workspace_bytes", "wan_patchify", "wan_time_embed",
            "wan_dit_block_forward", "wan_head", "wan_denoise_step", "wan_cache_bytes",
-           "wan_denoise_step_cached", "wan_timing_enable", "wan_timing_read")
+           "wan_denoise_step_cached", "wan_timing_enable", "wan_timing_read",
+           "wan_vae_param_count", "wan_vae_param_info", "wan_vae_blob_elems", "wan_vae_workspace_bytes",
+           "wan_vae_cache_bytes", "wan_vae_decode")
 
 CACHE_STORE = 1
 CACHE_REUSE_ATTN = 2
@@ -47,6 +49,15 @@ class WanShape(ctypes.Structure):
 
 
 _vp = ctypes.c_void_p
+
+
+class WanVaeShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("frames", "height", "width", "z_ch", "base", "n_res", "chunk")]
+
+
+class WanVaeParam(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("kind", ctypes.c_int), ("dims", ctypes.c_int * 5),
+                ("offset", ctypes.c_size_t), ("count", ctypes.c_size_t)]
 
 
 class WanBlockWeights(ctypes.Structure):
@@ -110,6 +121,21 @@ def load(path: str = LIB_PATH):
     lib.wan_timing_read.restype = ctypes.c_int
     lib.wan_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_longlong), ctypes.c_int]
+    vs = ctypes.POINTER(WanVaeShape)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.wan_vae_param_count.restype = ctypes.c_int
+    lib.wan_vae_param_count.argtypes = [vs, ip]
+    lib.wan_vae_param_info.restype = ctypes.c_int
+    lib.wan_vae_param_info.argtypes = [vs, ctypes.c_int, ctypes.POINTER(WanVaeParam)]
+    lib.wan_vae_blob_elems.restype = ctypes.c_size_t
+    lib.wan_vae_blob_elems.argtypes = [vs, ctypes.c_int, ip]
+    lib.wan_vae_workspace_bytes.restype = ctypes.c_size_t
+    lib.wan_vae_workspace_bytes.argtypes = [vs, ip]
+    lib.wan_vae_cache_bytes.restype = ctypes.c_size_t
+    lib.wan_vae_cache_bytes.argtypes = [vs, ip]
+    lib.wan_vae_decode.restype = ctypes.c_int
+    lib.wan_vae_decode.argtypes = [vs, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp, _vp,
+                                   ctypes.c_size_t, _vp]
     _lib = lib
     return lib
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwan.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "abi.hip"]
+SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "vae.hip", "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

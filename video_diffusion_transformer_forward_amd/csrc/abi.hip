@@ -4,10 +4,12 @@
 #include <string.h>
 
 #include <mutex>
+#include <string>
 #include <utility>
 #include <vector>
 
 #include "../../include/wan.h"
+#include "../../include/wan_vae.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -538,6 +540,323 @@ int run_head(const Dims& d, int Bb, const wan_model_weights* w, const float* x, 
   return WAN_OK;
 }
 
+
+// ======================================================================= Wan-VAE decoder
+// Layer list, parameter table, workspace plan and the launch sequence.
+
+struct VaeDims {
+  int T, H, W, zc, b, n_res, chunk;
+  int d[5];  // stage widths 4b, 4b, 4b, 2b, b
+};
+
+int vae_check(const wan_vae_shape* s, VaeDims* d) {
+  if (!s) return WAN_E_NULL;
+  if (s->frames < 1 || s->height < 1 || s->width < 1 || s->z_ch < 1 || s->z_ch > 32) return WAN_E_SHAPE;
+  if (s->base < 32 || s->base > 128 || s->base % 32 != 0 || s->n_res < 1 || s->n_res > 4) return WAN_E_SHAPE;
+  if (s->chunk < 1 || s->chunk > s->frames) return WAN_E_SHAPE;
+  if (256LL * s->chunk * s->height * s->width >= (1LL << 31)) return WAN_E_SHAPE;
+  if (d) {
+    d->T = s->frames;
+    d->H = s->height;
+    d->W = s->width;
+    d->zc = s->z_ch;
+    d->b = s->base;
+    d->n_res = s->n_res;
+    d->chunk = s->chunk;
+    const int b = s->base;
+    const int w[5] = {4 * b, 4 * b, 4 * b, 2 * b, b};
+    for (int i = 0; i < 5; ++i) d->d[i] = w[i];
+  }
+  return WAN_OK;
+}
+
+int vcs(int c) { return (c + 63) / 64 * 64; }  // channel stride of a buffer holding c channels
+
+struct VaeConvInfo {
+  int cout, kt, kh, kw, cin;
+  int level, in_cs;
+  size_t w_off, b_off;       // into the caller's blobs
+  int n_pad, cin_k;          // GEMM N and per-tap K (padded)
+  long long cache_off;       // into the feature cache, -1 without one
+  long long pad_off;         // padded weights (bf16) + bias (float) in the workspace, -1 if not padded
+};
+
+struct VaeTable {
+  std::vector<wan_vae_param> params;
+  std::vector<VaeConvInfo> convs;  // execution order
+  std::vector<size_t> norm_off;    // float-blob offsets of the RMSNorm scales, execution order
+  size_t w_elems = 0, f_elems = 0, cache_bytes = 0, pad_bytes = 0;
+};
+
+VaeTable vae_table(const VaeDims& d) {
+  VaeTable t;
+  auto lvl_hw = [&](int l, int& hp, int& wp) {
+    hp = (d.H << l) + 2;
+    wp = (d.W << l) + 2;
+  };
+  auto add_param = [&](const char* name, int kind, std::initializer_list<int> dims, size_t count) {
+    wan_vae_param p;
+    memset(&p, 0, sizeof(p));
+    strncpy(p.name, name, sizeof(p.name) - 1);
+    p.kind = kind;
+    int i = 0;
+    for (int v : dims) p.dims[i++] = v;
+    size_t& off = kind == 0 ? t.w_elems : t.f_elems;
+    off = (off + 63) / 64 * 64;
+    p.offset = off;
+    p.count = count;
+    off += count;
+    t.params.push_back(p);
+    return p.offset;
+  };
+  auto add_norm = [&](const std::string& name, int c) {
+    t.norm_off.push_back(add_param(name.c_str(), 2, {c}, (size_t)c));
+  };
+  auto add_conv = [&](const std::string& name, int cout, int kt, int kh, int kw, int cin, int level, int in_cs) {
+    VaeConvInfo c;
+    c.cout = cout; c.kt = kt; c.kh = kh; c.kw = kw; c.cin = cin; c.level = level; c.in_cs = in_cs;
+    c.w_off = add_param(name.c_str(), 0, {cout, kt, kh, kw, cin}, (size_t)cout * kt * kh * kw * cin);
+    c.b_off = add_param((name + ".bias").c_str(), 1, {cout}, (size_t)cout);
+    c.n_pad = vcs(cout);
+    c.cin_k = (cin + 31) / 32 * 32;
+    c.cache_off = -1;
+    if (kt > 1) {
+      int hp, wp;
+      lvl_hw(level, hp, wp);
+      c.cache_off = (long long)t.cache_bytes;
+      t.cache_bytes += al((size_t)(kt - 1) * hp * wp * in_cs * 2);
+    }
+    c.pad_off = -1;
+    if (c.n_pad != cout || c.cin_k != cin) {
+      c.pad_off = (long long)t.pad_bytes;
+      t.pad_bytes += al((size_t)c.n_pad * kt * kh * kw * c.cin_k * 2) + al((size_t)c.n_pad * 4);
+    }
+    t.convs.push_back(c);
+  };
+  auto add_res = [&](const std::string& pre, int cin, int cout, int level) {
+    add_norm(pre + ".norm_a", cin);
+    add_conv(pre + ".conv_a", cout, 3, 3, 3, cin, level, vcs(cin));
+    add_norm(pre + ".norm_b", cout);
+    add_conv(pre + ".conv_b", cout, 3, 3, 3, cout, level, vcs(cout));
+    if (cin != cout) add_conv(pre + ".skip", cout, 1, 1, 1, cin, level, vcs(cin));
+  };
+  add_conv("conv_in", d.d[0], 3, 3, 3, d.zc, 0, 32);
+  for (int i = 0; i < 2; ++i) add_res("mid." + std::to_string(i), d.d[0], d.d[0], 0);
+  for (int s = 0; s < 4; ++s) {
+    const int cin = d.d[s], cout = d.d[s + 1];
+    for (int j = 0; j < d.n_res; ++j)
+      add_res("up." + std::to_string(s) + ".res." + std::to_string(j), j == 0 ? cin : cout, cout, s);
+    if (s < 2) add_conv("up." + std::to_string(s) + ".time_conv", 2 * cout, 3, 1, 1, cout, s, vcs(cout));
+    if (s < 3) add_conv("up." + std::to_string(s) + ".space_conv", cout, 1, 3, 3, cout, s + 1, vcs(cout));
+  }
+  add_norm("head.norm", d.d[4]);
+  add_conv("head.conv", 3, 3, 3, 3, d.d[4], 3, vcs(d.d[4]));
+  return t;
+}
+
+// Frames held per level for a call of n latent frames: level 0 also holds the
+// time-doubled frames of stage 0, level 1 those of stage 1.
+void vae_frames(int n, bool first, int f[4]) {
+  const int f1 = first ? 2 * n - 1 : 2 * n;
+  const int f2 = first ? 4 * n - 3 : 4 * n;
+  f[0] = n;
+  f[1] = f1;
+  f[2] = f2;
+  f[3] = f2;
+}
+
+struct VaePlan {
+  size_t buf[4][4];     // four buffers per level
+  size_t buf_bytes[4];
+  int cap[4], cs[4];    // frame capacity (with the two cache frames) and channel stride per level
+  size_t pad;           // padded weights
+  size_t total;
+};
+
+VaePlan vae_plan(const VaeDims& d, const VaeTable& t) {
+  VaePlan p;
+  const int capf[4] = {2 * d.chunk, 4 * d.chunk, 4 * d.chunk, 4 * d.chunk};
+  const int cs[4] = {vcs(d.d[0]), vcs(d.d[1]), vcs(d.d[2]), vcs(d.d[3]) > vcs(d.d[4]) ? vcs(d.d[3]) : vcs(d.d[4])};
+  size_t off = 0;
+  for (int l = 0; l < 4; ++l) {
+    p.cap[l] = capf[l] + 2;
+    p.cs[l] = l == 0 && cs[0] < 32 ? 32 : cs[l];
+    const size_t hp = (size_t)(d.H << l) + 2, wp = (size_t)(d.W << l) + 2;
+    p.buf_bytes[l] = al((size_t)p.cap[l] * hp * wp * p.cs[l] * 2);
+    for (int k = 0; k < 4; ++k) {
+      p.buf[l][k] = off;
+      off += p.buf_bytes[l];
+    }
+  }
+  p.pad = off;
+  off += t.pad_bytes;
+  p.total = off;
+  return p;
+}
+
+struct VaeAct {
+  int l, k;    // level, buffer index
+  int c, cs;   // channels, channel stride
+  int nf;      // frames
+};
+
+int vae_run(const VaeDims& d, const VaeTable& tab, const VaePlan& pl, const void* wblob, const float* fblob,
+            const float* z, int t0, int n, char* cache, float* video, char* ws, hipStream_t st) {
+  const bool first = t0 == 0;
+  const bf16* W = static_cast<const bf16*>(wblob);
+  auto buf = [&](int l, int k) { return ws + pl.buf[l][k]; };
+  auto hp = [&](int l) { return (d.H << l) + 2; };
+  auto wp = [&](int l) { return (d.W << l) + 2; };
+  auto frame_bytes = [&](int l, int cs) { return (size_t)hp(l) * wp(l) * cs * 2; };
+
+  // padded weights
+  for (const VaeConvInfo& c : tab.convs) {
+    if (c.pad_off < 0) continue;
+    const int taps = c.kt * c.kh * c.kw;
+    char* wp_ = ws + pl.pad + c.pad_off;
+    float* bp = reinterpret_cast<float*>(wp_ + al((size_t)c.n_pad * taps * c.cin_k * 2));
+    HIP_TRY(launch_vae_pad_weight(W + c.w_off, fblob + c.b_off, wp_, bp, c.cout, c.n_pad, taps, c.cin, c.cin_k, st));
+  }
+  if (first) HIP_TRY(hipMemsetAsync(cache, 0, tab.cache_bytes, st));
+
+  size_t conv_i = 0, norm_i = 0;
+  // one convolution: in (level l, stride in.cs, in.nf frames); rows of frames [t_in0, t_in0 + rows_f)
+  auto conv = [&](const VaeAct& in, int rows_f, int t_in0, void* out, int out_cs, int of0, int ofs, int split,
+                  const void* res, int epi, long long plane) -> int {
+    const VaeConvInfo& c = tab.convs[conv_i++];
+    const int l = in.l;
+    char* ib = buf(l, in.k);
+    // the spatial taps read the one-voxel border of the input frames as zero padding: a
+    // buffer holds other tensors (and strides) earlier in the call, so clear it here; the
+    // two leading frames come from the cache, whose frames were saved with clear borders
+    HIP_TRY(launch_vae_border(ib + 2 * frame_bytes(l, in.cs), in.nf, hp(l), wp(l), in.cs, st));
+    if (c.cache_off >= 0) HIP_TRY(copy_async(ib, cache + c.cache_off, 2 * frame_bytes(l, in.cs), st));
+    const int taps = c.kt * c.kh * c.kw;
+    GemmArgs g;
+    g.M = rows_f * (d.H << l) * (d.W << l);
+    g.N = c.n_pad;
+    g.K = taps * c.cin_k;
+    g.A = ib;
+    g.lda = in.cs;
+    if (c.pad_off >= 0) {
+      char* wp_ = ws + pl.pad + c.pad_off;
+      g.Wt = wp_;
+      g.bias = reinterpret_cast<const float*>(wp_ + al((size_t)c.n_pad * taps * c.cin_k * 2));
+    } else {
+      g.Wt = W + c.w_off;
+      g.bias = fblob + c.b_off;
+    }
+    g.ldw = g.K;
+    g.cv_h = d.H << l;
+    g.cv_w = d.W << l;
+    g.cv_hp = hp(l);
+    g.cv_wp = wp(l);
+    g.cv_t0 = t_in0;
+    g.cv_kpt = c.cin_k / 32;
+    for (int dt = 0; dt < c.kt; ++dt)
+      for (int dh = 0; dh < c.kh; ++dh)
+        for (int dw = 0; dw < c.kw; ++dw) {
+          const int ft = dt + (3 - c.kt), fh = dh + (3 - c.kh) / 2, fw = dw + (3 - c.kw) / 2;
+          g.tap_off[(dt * c.kh + dh) * c.kw + dw] = (((long long)ft * hp(l) + fh) * wp(l) + fw) * in.cs;
+        }
+    g.cv_of0 = of0;
+    g.cv_ofs = ofs;
+    if (split > 0) g.cv_split = split;
+    g.cv_res = res;
+    g.cv_nout = 3;
+    g.C = out;
+    g.ldc = epi == EPI_CONV_VIDEO ? plane : out_cs;
+    HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<bf16>(g, LOAD_CONV, epi, st); }));
+    if (c.cache_off >= 0)
+      HIP_TRY(copy_async(cache + c.cache_off, ib + (size_t)in.nf * frame_bytes(l, in.cs), 2 * frame_bytes(l, in.cs), st));
+    return WAN_OK;
+  };
+  auto norm = [&](const VaeAct& in, int k_out) -> int {
+    const float* gsc = fblob + tab.norm_off[norm_i++];
+    const int l = in.l;
+    HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] {
+      return launch_vae_rms_silu(buf(l, in.k), buf(l, k_out), gsc, in.c, in.cs, in.nf, d.H << l, d.W << l, st);
+    }));
+    return WAN_OK;
+  };
+  auto free_buf = [&](int a, int b = -1, int c = -1) {
+    for (int k = 0; k < 4; ++k)
+      if (k != a && k != b && k != c) return k;
+    return -1;
+  };
+  int rc;
+  // residual block: x -> (in place, or into a new buffer when the width changes)
+  auto res = [&](VaeAct& x, int cout) -> int {
+    const int l = x.l;
+    const int kn = free_buf(x.k), kh = free_buf(x.k, kn), ks = free_buf(x.k, kn, kh);
+    if ((rc = norm(x, kn))) return rc;
+    VaeAct nv{l, kn, x.c, x.cs, x.nf};
+    if ((rc = conv(nv, x.nf, 0, buf(l, kh), vcs(cout), 0, 1, 0, nullptr, EPI_CONV, 0))) return rc;
+    VaeAct hv{l, kh, cout, vcs(cout), x.nf};
+    if ((rc = norm(hv, kn))) return rc;
+    VaeAct n2{l, kn, cout, vcs(cout), x.nf};
+    if (x.c == cout) {
+      if ((rc = conv(n2, x.nf, 0, buf(l, x.k), x.cs, 0, 1, 0, buf(l, x.k), EPI_CONV, 0))) return rc;
+    } else {
+      // the block's second convolution comes before its shortcut in execution order
+      const size_t conv_b = conv_i;
+      conv_i = conv_b + 1;  // shortcut first, into ks
+      if ((rc = conv(x, x.nf, 0, buf(l, ks), vcs(cout), 0, 1, 0, nullptr, EPI_CONV, 0))) return rc;
+      const size_t after = conv_i;
+      conv_i = conv_b;
+      if ((rc = conv(n2, x.nf, 0, buf(l, ks), vcs(cout), 0, 1, 0, buf(l, ks), EPI_CONV, 0))) return rc;
+      conv_i = after;
+      x.k = ks;
+      x.c = cout;
+      x.cs = vcs(cout);
+    }
+    return WAN_OK;
+  };
+
+  int f[4];
+  vae_frames(n, first, f);
+  VaeAct x{0, 0, d.zc, 32, n};
+  HIP_TRY(launch_vae_latent(z, buf(0, 0), d.zc, n, d.H, d.W, 32, st));
+  {
+    const int k = free_buf(0);
+    if ((rc = conv(x, n, 0, buf(0, k), vcs(d.d[0]), 0, 1, 0, nullptr, EPI_CONV, 0))) return rc;
+    x = VaeAct{0, k, d.d[0], vcs(d.d[0]), n};
+  }
+  for (int i = 0; i < 2; ++i)
+    if ((rc = res(x, d.d[0]))) return rc;
+  for (int s = 0; s < 4; ++s) {
+    for (int j = 0; j < d.n_res; ++j)
+      if ((rc = res(x, d.d[s + 1]))) return rc;
+    if (s < 2) {
+      // time doubling at this level's resolution: frames t >= (first ? 1 : 0) -> two frames each
+      const int l = x.l, kt_ = free_buf(x.k);
+      const int t0r = first ? 1 : 0;
+      if ((rc = conv(x, x.nf - t0r, t0r, buf(l, kt_), x.cs, t0r, 2, x.c, nullptr, EPI_CONV, 0))) return rc;
+      if (first) HIP_TRY(copy_async(buf(l, kt_) + 2 * frame_bytes(l, x.cs), buf(l, x.k) + 2 * frame_bytes(l, x.cs),
+                                    frame_bytes(l, x.cs), st));
+      x.k = kt_;
+      x.nf = f[s + 1];
+    }
+    if (s < 3) {
+      const int l = x.l, ku = 0, kv = 1;
+      HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] {
+        return launch_vae_up_space(buf(l, x.k), buf(l + 1, ku), x.nf, d.H << l, d.W << l, x.cs, st);
+      }));
+      VaeAct u{l + 1, ku, x.c, x.cs, x.nf};
+      if ((rc = conv(u, x.nf, 0, buf(l + 1, kv), x.cs, 0, 1, 0, nullptr, EPI_CONV, 0))) return rc;
+      x = VaeAct{l + 1, kv, x.c, x.cs, x.nf};
+    }
+  }
+  // head
+  {
+    const int kn = free_buf(x.k);
+    if ((rc = norm(x, kn))) return rc;
+    VaeAct nv{3, kn, x.c, x.cs, x.nf};
+    const long long plane = (long long)x.nf * (d.H << 3) * (d.W << 3);
+    if ((rc = conv(nv, x.nf, 0, video, 0, 0, 1, 0, nullptr, EPI_CONV_VIDEO, plane))) return rc;
+  }
+  return conv_i == tab.convs.size() && norm_i == tab.norm_off.size() ? WAN_OK : WAN_E_SHAPE;
+}
 }  // namespace
 }  // namespace wan
 
@@ -732,6 +1051,66 @@ int wan_denoise_step_cached(const wan_shape* s, const wan_model_weights* w, floa
   if (!cache) return WAN_E_NULL;
   return step_entry(s, w, z, cond, ctx_cond, ctx_null, timestep, dt, guide_scale, cache_mode, cache, cache_bytes_,
                     ws, ws_bytes, stream);
+}
+
+int wan_vae_param_count(const wan_vae_shape* s, int* status) {
+  VaeDims d;
+  const int rc = vae_check(s, &d);
+  if (status) *status = rc;
+  return rc == WAN_OK ? (int)vae_table(d).params.size() : 0;
+}
+
+int wan_vae_param_info(const wan_vae_shape* s, int index, wan_vae_param* out) {
+  VaeDims d;
+  int rc = vae_check(s, &d);
+  if (rc) return rc;
+  if (!out) return WAN_E_NULL;
+  const VaeTable t = vae_table(d);
+  if (index < 0 || index >= (int)t.params.size()) return WAN_E_ENTRY;
+  *out = t.params[index];
+  return WAN_OK;
+}
+
+size_t wan_vae_blob_elems(const wan_vae_shape* s, int which, int* status) {
+  VaeDims d;
+  int rc = vae_check(s, &d);
+  if (rc == WAN_OK && which != 0 && which != 1) rc = WAN_E_ENTRY;
+  if (status) *status = rc;
+  if (rc) return 0;
+  const VaeTable t = vae_table(d);
+  return which == 0 ? t.w_elems : t.f_elems;
+}
+
+size_t wan_vae_workspace_bytes(const wan_vae_shape* s, int* status) {
+  VaeDims d;
+  const int rc = vae_check(s, &d);
+  if (status) *status = rc;
+  if (rc) return 0;
+  const VaeTable t = vae_table(d);
+  return vae_plan(d, t).total;
+}
+
+size_t wan_vae_cache_bytes(const wan_vae_shape* s, int* status) {
+  VaeDims d;
+  const int rc = vae_check(s, &d);
+  if (status) *status = rc;
+  return rc == WAN_OK ? vae_table(d).cache_bytes : 0;
+}
+
+int wan_vae_decode(const wan_vae_shape* s, const void* weights, const float* fparams, const float* z, int t0, int n,
+                   void* cache, size_t cache_bytes_, float* video, void* ws, size_t ws_bytes, void* stream) {
+  VaeDims d;
+  int rc = vae_check(s, &d);
+  if (rc) return rc;
+  if ((rc = check_ptrs({weights, fparams, z, cache, video}))) return rc;
+  if (n < 1 || n > d.chunk || t0 < 0 || t0 + n > d.T) return WAN_E_SHAPE;
+  const VaeTable t = vae_table(d);
+  const VaePlan p = vae_plan(d, t);
+  if (cache_bytes_ < t.cache_bytes) return WAN_E_WORKSPACE;
+  if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
+  if ((rc = check_device())) return rc;
+  return vae_run(d, t, p, weights, fparams, z, t0, n, static_cast<char*>(cache), video, static_cast<char*>(ws),
+                 static_cast<hipStream_t>(stream));
 }
 
 int wan_timing_enable(int on) {

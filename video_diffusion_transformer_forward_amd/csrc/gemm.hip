@@ -295,7 +295,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
     wait_vmcnt<0>();
     __syncthreads();
-  } else if constexpr (LOADER == LOAD_PLAIN) {
+  } else if constexpr (LOADER == LOAD_PLAIN || LOADER == LOAD_CONV) {
     // ---- LDS-DMA ring.  One wave instruction fills 1 KB = RPD tile rows; lane
     // l writes the l-th 16 bytes, so the chunk swizzle is applied to the global
     // address each lane reads.
@@ -310,10 +310,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     for (int i = 0; i < NA; ++i) {
       const int rt = (wave * NA + i) * RPD + rlow;  // row within the tile
       const int r = min(m0 + rt, g.M - 1);
-      const int bb = r / g.a_rpb;
-      int t = r - bb * g.a_rpb;
-      if (g.a_valid > 0) t = min(t, g.a_valid - 1);  // padding rows of a padded row pitch
-      a_src[i] = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda + col_off(rt);
+      if constexpr (LOADER == LOAD_CONV) {
+        // output voxel (t, h, w) of the chunk; the taps add their offsets per k-tile
+        const int hw = g.cv_h * g.cv_w;
+        const int tv = r / hw, rem = r - tv * hw;
+        const int hv = rem / g.cv_w, wv = rem - hv * g.cv_w;
+        a_src[i] = reinterpret_cast<const T*>(g.A) +
+                   (((long long)(tv + g.cv_t0) * g.cv_hp + hv) * g.cv_wp + wv) * g.lda + col_off(rt);
+      } else {
+        const int bb = r / g.a_rpb;
+        int t = r - bb * g.a_rpb;
+        if (g.a_valid > 0) t = min(t, g.a_valid - 1);  // padding rows of a padded row pitch
+        a_src[i] = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda + col_off(rt);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -323,9 +332,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     auto issue = [&](int kt) {
       unsigned char* base = smem_raw + (size_t)(kt % NST) * C::STAGE * sizeof(Chunk<T>);
       const int koff = kt * BK;
+      long long aoff = koff;
+      if constexpr (LOADER == LOAD_CONV) {
+        const int tap = kt / g.cv_kpt;
+        aoff = g.tap_off[tap] + (long long)(kt - tap * g.cv_kpt) * BK;
+      }
 #pragma unroll
       for (int i = 0; i < NA; ++i)
-        __builtin_amdgcn_global_load_lds(a_src[i] + koff, (lds_void*)(base + (size_t)(wave * NA + i) * 1024), 16,
+        __builtin_amdgcn_global_load_lds(a_src[i] + aoff, (lds_void*)(base + (size_t)(wave * NA + i) * 1024), 16,
                                          0, 0);
       unsigned char* bbase = base + (size_t)BM * CPR * sizeof(Chunk<T>);
 #pragma unroll
@@ -599,7 +613,34 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             v[4 + u] += b1[u];
           }
         }
-        if constexpr (EPI == EPI_STORE_GELU8) {
+        if constexpr (EPI == EPI_CONV || EPI == EPI_CONV_VIDEO) {
+          const int hw = g.cv_h * g.cv_w;
+          const int tv = row / hw, rem = row - tv * hw;
+          const int hv = rem / g.cv_w, wv = rem - hv * g.cv_w;
+          if constexpr (EPI == EPI_CONV) {
+            int ch = n, fr = g.cv_of0 + g.cv_ofs * tv;
+            if (n >= g.cv_split) {
+              ch = n - g.cv_split;
+              fr += 1;
+            }
+            const long long off = (((long long)(fr + 2) * g.cv_hp + hv + 1) * g.cv_wp + wv + 1) * g.ldc + ch;
+            if (g.cv_res) {
+              Chunk<T> rc;
+              rc.load(reinterpret_cast<const T*>(g.cv_res) + off);
+              const bf16x8 r8 = as_bf16x8(rc.v);
+#pragma unroll
+              for (int u = 0; u < 8; ++u) v[u] += (float)r8[u];
+            }
+            Chunk<T> c;
+            pack8(c, v);
+            c.store(reinterpret_cast<T*>(g.C) + off);
+          } else {
+            const long long px = (long long)(g.cv_of0 + tv) * hw + rem;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (n + u < g.cv_nout) reinterpret_cast<float*>(g.C)[(long long)(n + u) * g.ldc + px] = v[u];
+          }
+        } else if constexpr (EPI == EPI_STORE_GELU8) {
           // GELU, then e4m3 with one power-of-two scale per (row, 128-column block):
           // the 16 lanes of this row within the 128-column slab hold the block
 #pragma unroll
@@ -713,7 +754,8 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   using C = Gemm<T, BM, BN, WM, WN, NST, RB, LOADER, EPI>;
   static_assert(OCC * C::LDS_BYTES <= 160 * 1024, "occupancy exceeds the LDS");
   if (g.N % BN != 0) return hipErrorInvalidValue;
-  if ((LOADER == LOAD_PLAIN || LOADER == LOAD_FP8) && g.K % C::BK != 0) return hipErrorInvalidValue;
+  if ((LOADER == LOAD_PLAIN || LOADER == LOAD_FP8 || LOADER == LOAD_CONV) && g.K % C::BK != 0)
+    return hipErrorInvalidValue;
   auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, RB, OCC, LOADER, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -760,6 +802,22 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
   if (loader == LOAD_PLAIN && g.K % BK != 0) return hipErrorInvalidValue;
   if (loader == LOAD_PATCH) {
     if (epi == EPI_STORE_F32) return launch_by_n<T, LOAD_PATCH, EPI_STORE_F32>(g, st);
+    return hipErrorInvalidValue;
+  }
+  if (loader == LOAD_CONV) {
+    // bf16 convolutions: whole 32-channel k-tiles per tap
+    if constexpr (sizeof(T) == 2) {
+      if (g.K % 32 != 0 || g.cv_kpt < 1 || g.K / 32 > g.cv_kpt * CONV_MAX_TAPS || g.K % (32 * g.cv_kpt) != 0 ||
+          g.cv_h < 1 || g.cv_w < 1)
+        return hipErrorInvalidValue;
+      if (epi == EPI_CONV) {
+        if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_CONV, EPI_CONV>(g, st);
+        if (g.N % 128 == 0) return launch_cfg<T, 256, 128, 2, 2, 3, 64, 2, LOAD_CONV, EPI_CONV>(g, st);
+        if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOAD_CONV, EPI_CONV>(g, st);
+      } else if (epi == EPI_CONV_VIDEO) {
+        if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOAD_CONV, EPI_CONV_VIDEO>(g, st);
+      }
+    }
     return hipErrorInvalidValue;
   }
   if (loader == LOAD_FP8) {

@@ -9,11 +9,23 @@ namespace wan {
 // LOAD_FP8 (T = bf16 output type): A and W are e4m3 bytes with one power-of-two
 // scale byte (exponent + 127) per 128-element block along K: A scales at
 // a_scale[blk * a_sld + r] for GEMM row r, W scales at w_scale[blk * N + n]
-enum Loader { LOAD_PLAIN = 0, LOAD_PATCH = 1, LOAD_FP8 = 2 };
+// LOAD_CONV (bf16): implicit GEMM of a convolution over a padded channels-last
+// buffer [frames][cv_hp][cv_wp][lda]: row r is output voxel (t, h, w) of a
+// (cv_h x cv_w) frame, t = r / (cv_h cv_w); column k = tap * (cv_kpt * 32) + c reads
+// A + ((t + cv_t0) * cv_hp + h) * cv_wp + w) * lda + tap_off[tap] + c
+enum Loader { LOAD_PLAIN = 0, LOAD_PATCH = 1, LOAD_FP8 = 2, LOAD_CONV = 3 };
 // EPI_STORE_GELU8: GELU, then e4m3 bytes at C + r * ldc + n with one scale byte per
 // (row, 128-column block) at c_scale[(n / 128) * c_sld + r]
+// EPI_CONV (LOAD_CONV): bf16 into a padded channels-last buffer with two leading
+// cache frames: voxel (t, h, w), column n -> frame cv_of0 + cv_ofs * t (+1 for
+// n >= cv_split, channel n - cv_split), stored at
+// C + (((frame + 2) * cv_hp + h + 1) * cv_wp + w + 1) * ldc + channel, plus cv_res
+// (same layout) when non-null.  EPI_CONV_VIDEO: float32 video planes
+// C[n][cv_of0 + t][h][w] (plane stride ldc) for n < cv_nout.
 enum Epi { EPI_STORE = 0, EPI_STORE_GELU = 1, EPI_STORE_F32 = 2, EPI_RESID = 3, EPI_PACK = 4, EPI_PACK8 = 5,
-           EPI_STORE_GELU8 = 6 };
+           EPI_STORE_GELU8 = 6, EPI_CONV = 7, EPI_CONV_VIDEO = 8 };
+
+constexpr int CONV_MAX_TAPS = 27;
 
 // C[M][N] = A[M][K] * W[N][K]^T + bias, with an epilogue selected by `epi`.
 struct GemmArgs {
@@ -28,6 +40,11 @@ struct GemmArgs {
   const unsigned char* a_scale = nullptr;
   long long a_sld = 0;
   const unsigned char* w_scale = nullptr;
+  // LOAD_CONV / EPI_CONV geometry
+  int cv_h = 0, cv_w = 0, cv_hp = 0, cv_wp = 0, cv_t0 = 0, cv_kpt = 1;
+  int cv_of0 = 0, cv_ofs = 1, cv_split = 1 << 30, cv_nout = 0;
+  const void* cv_res = nullptr;
+  long long tap_off[CONV_MAX_TAPS] = {};
   // A operand (LOAD_PATCH): (1,2,2) patches of [z ; cond], token rows of `zb_count` videos
   const float* z = nullptr;
   const float* cond = nullptr;
@@ -123,6 +140,16 @@ hipError_t launch_gemv(const void* Wt, const float* bias, const float* x, float 
 // branch and p_null (default: p rows [B*L, 2*B*L)) the unconditional one.
 hipError_t launch_unpatch(const float* p, float* out, int B, int C, int F, int H, int W, int step, float dt,
                           float guide, hipStream_t st, const float* p_null = nullptr);
+
+// Wan-VAE decoder helpers over padded channels-last bf16 frame buffers
+// [2 + frames][H + 2][W + 2][Cs] (two leading cache frames, one-voxel zero border)
+hipError_t launch_vae_latent(const float* z, void* buf, int zc, int n, int H, int W, int Cs, hipStream_t st);
+hipError_t launch_vae_rms_silu(const void* in, void* out, const float* g, int C, int Cs, int n, int H, int W,
+                               hipStream_t st);
+hipError_t launch_vae_up_space(const void* in, void* out, int n, int H, int W, int Cs, hipStream_t st);
+hipError_t launch_vae_border(void* buf, int frames, int Hp, int Wp, int Cs, hipStream_t st);
+hipError_t launch_vae_pad_weight(const void* W, const float* b, void* Wp, float* bp, int Cout, int N, int taps, int Cin,
+                                 int Cink, hipStream_t st);
 
 // copy helper (device to device, on the stream)
 hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t st);
