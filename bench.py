@@ -94,6 +94,63 @@ def time_block(bcfg: S.WanConfig, reps: int = 5) -> dict:
             "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "seq_len": bcfg.seq_len, "dim": bcfg.dim}
 
 
+def vae_flops(vcfg) -> float:
+    """Algorithmic FLOPs of one whole-video decode: 2 x voxels x C_out x (taps x C_in) per convolution."""
+    from video_diffusion_transformer_forward_amd import vae_synth as VS
+    T, H, W = vcfg.frames, vcfg.height, vcfg.width
+    frames = [T, 2 * T - 1, 4 * T - 3, 4 * T - 3]   # per level: latent, after each time doubling
+    total = 0.0
+    for name, shape in VS.vae_param_shapes(vcfg):
+        if len(shape) != 5:
+            continue
+        cout, kt, kh, kw, cin = shape
+        if name == "conv_in" or name.startswith("mid."):
+            lvl = 0
+        elif name.startswith("head."):
+            lvl = 3
+        else:
+            s = int(name.split(".")[1])
+            lvl = s + 1 if name.endswith("space_conv") else s
+        nf = frames[lvl]
+        if name.endswith("time_conv"):
+            nf = frames[lvl] - 1          # the first frame passes through
+        vox = nf * (H << lvl) * (W << lvl)
+        total += 2.0 * vox * cout * kt * kh * kw * cin
+    return total
+
+
+def time_vae(name: str = "vae_480p", reps: int = 3) -> dict:
+    """Whole-video decode of the 81-frame 480p latent (one call), timed with torch events."""
+    import torch
+    import video_diffusion_transformer_forward_amd as W
+    from video_diffusion_transformer_forward_amd import vae_synth as VS
+    vcfg = VS.get_vae_config(name)
+    sh = W.vae_shape_of(vcfg)
+    dev = W.VaeDevice(sh, VS.vae_params(vcfg))
+    ws = W.vae_workspace(sh)
+    cache = W.vae_cache(sh)
+    z = torch.from_numpy(VS.vae_latent(vcfg)).cuda()
+    video = torch.empty((3, vcfg.out_frames, vcfg.out_height, vcfg.out_width), dtype=torch.float32, device="cuda")
+    W.vae_decode(sh, dev, z, 0, vcfg.frames, cache, video, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        W.vae_decode(sh, dev, z, 0, vcfg.frames, cache, video, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    assert bool(torch.isfinite(video).all())
+    fl = vae_flops(vcfg)
+    out = {"workload": f"{name}: latent 16x{vcfg.frames}x{vcfg.height}x{vcfg.width} -> video 3x{vcfg.out_frames}x"
+                       f"{vcfg.out_height}x{vcfg.out_width}, widths {list(vcfg.dims)}, {vcfg.n_res} residual blocks "
+                       f"per stage, one call",
+           "ms_per_video": round(ms, 2), "tflop": round(fl / 1e12, 2),
+           "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+           "workspace_gb": round(ws.numel() / 1e9, 2)}
+    del ws, cache, video, dev
+    torch.cuda.empty_cache()
+    return out
+
+
 def attn_traffic_bytes():
     """Counted bytes per self-attention launch, or None once its sources differ from the measured ones."""
     import hashlib
@@ -151,6 +208,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-modes", action="store_true", help="skip timing the diffusion-cache step modes")
     ap.add_argument("--no-qk8", action="store_true", help="skip timing the step in the 8-bit forms")
+    ap.add_argument("--no-vae", action="store_true", help="skip timing the 480p x 81-frame VAE decode")
+    ap.add_argument("--vae-only", action="store_true",
+                    help="time only the VAE decode and print its JSON object (for profiling runs)")
     ap.add_argument("--block-configs", default="",
                     help="comma-separated block configurations to time one block forward of "
                          "(e.g. wan13b_block,wan14b_720p_block,wan14b_i2v_block); reported under 'blocks'")
@@ -167,6 +227,9 @@ def main():
     import video_diffusion_transformer_forward_amd as W
     from video_diffusion_transformer_forward_amd import _native as N
 
+    if args.vae_only:
+        print(json.dumps({"vae_decode": time_vae()}), flush=True)
+        return
     cfg = S.get_config(args.config)
     assert cfg.mode == "bf16"
     print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
@@ -330,6 +393,9 @@ def main():
             "ms_per_step": cache_ms, "cache_gb": cache_gb,
             "note": "one CFG step per mode after a store step; a reuse step skips the QKV projection and "
                     "self-attention (reuse_attn) and/or the unconditional branch (reuse_uncond)"}
+    if not args.no_vae:
+        print("[bench] vae decode", file=sys.stderr, flush=True)
+        out["vae_decode"] = time_vae()
     if args.block_configs:
         out["blocks"] = {}
         for name in [c for c in args.block_configs.split(",") if c]:

@@ -813,6 +813,8 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
       if (epi == EPI_CONV) {
         if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_CONV, EPI_CONV>(g, st);
         if (g.N % 128 == 0) return launch_cfg<T, 256, 128, 2, 2, 3, 64, 2, LOAD_CONV, EPI_CONV>(g, st);
+        // 192-wide outputs: 128x192 tiles of 4 waves (64x96 each), two workgroups per CU
+        if (g.N % 192 == 0) return launch_cfg<T, 128, 192, 2, 2, 4, 64, 2, LOAD_CONV, EPI_CONV>(g, st);
         if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOAD_CONV, EPI_CONV>(g, st);
       } else if (epi == EPI_CONV_VIDEO) {
         if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOAD_CONV, EPI_CONV_VIDEO>(g, st);
