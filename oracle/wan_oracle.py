@@ -371,7 +371,8 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
         x <- x + g2 * FFN(LN(x) (1 + sc2) + sh2)
 
     x: (B, L, D); mod: (B, 6, D) or (6, D) (shift1, scale1, gate1, shift2,
-    scale2, gate2); ctx: (B, L_img + L_txt, D).
+    scale2, gate2), or (B, L, 6, D) for a modulation per token (the streaming
+    queue's per-frame noise levels); ctx: (B, L_img + L_txt, D).
     rows: if given, return only those tokens' outputs (the keys and values of
     self-attention still come from every token) -> (B, len(rows), D).
     attn / record: see self_attention (diffusion cache); qk8: 8-bit q k^T in self-attention;
@@ -381,8 +382,13 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
     mod = f64(mod)
     if mod.ndim == 2:
         mod = mod[None]
-    sh1, sc1, g1, sh2, sc2, g2 = [mod[:, i][:, None, :] for i in range(6)]
+    if mod.ndim == 4:                      # per token: (B, L, 6, D)
+        sh1, sc1, g1, sh2, sc2, g2 = [mod[:, :, i] for i in range(6)]
+    else:
+        sh1, sc1, g1, sh2, sc2, g2 = [mod[:, i][:, None, :] for i in range(6)]
     m_all = modulate(layer_norm(x), sh1, sc1)
+    if mod.ndim == 4 and rows is not None:
+        g1, sh2, sc2, g2 = [a[:, rows] for a in (g1, sh2, sc2, g2)]
     xr = x if rows is None else x[:, rows]
     xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record, qk8, fp8)
     xr = xr + cross_attention(layer_norm(xr), ctx, w, heads, img_len, fp8)
@@ -480,3 +486,38 @@ def denoise_step_cached(z, cond, ctx_cond, ctx_null, model_w, blocks_w, heads, t
             v_u = dit_forward(z, cond, ctx_null, model_w, blocks_w, heads, tau, img_len,
                               attn_cache=cache["attn_u"] if reuse_attn else None, qk8=qk8, fp8=fp8)
     return euler_update(z, cfg_combine(v_c, v_u, guide_scale), dt)
+
+
+# --------------------------------------------------------------------------- streaming queue
+def stream_tick(window, ctx, model_w, blocks_w, heads, taus, dts, group, noise_in, qk8=False):
+    """One tick of the streaming denoise queue ([P1] 6.2 Streamer: a sliding
+    temporal window makes arbitrarily long videos; 6.3: with a distilled
+    consistency model the classifier-free guidance is folded into the model and
+    a frame needs four sampling steps).  Reading taken: the window holds K slots
+    of `group` latent frames each, slot 0 the oldest; slot k sits at noise level
+    taus[k] (its own time modulation, the same for all of its tokens) and moves by
+    dts[k] in one Euler step of the conditional velocity (no guidance); the
+    whole window attends as one video (RoPE positions are window positions).
+    After the step slot 0 leaves the queue and `noise_in` enters as the newest
+    slot.
+
+    window (1, 16, K*group, H, W); noise_in (1, 16, group, H, W).
+    Returns (new window, emitted frames (1, 16, group, H, W))."""
+    window = f64(window)
+    B, C, F, H, W = window.shape
+    K = len(taus)
+    assert B == 1 and F == K * group and len(dts) == K
+    grid = (F, H // 2, W // 2)
+    per_frame = (H // 2) * (W // 2)
+    mods = [time_modulation(t, model_w["t1_w"], model_w["t1_b"], model_w["t2_w"], model_w["t2_b"],
+                            model_w["m_w"], model_w["m_b"]) for t in taus]          # K x (6, D)
+    mod_tok = np.stack([mods[f // group] for f in range(F) for _ in range(per_frame)])[None]   # (1, L, 6, D)
+    x = patchify(window, None, model_w["pe_w"], model_w["pe_b"])
+    for w in blocks_w:
+        x = dit_block(x, mod_tok, ctx, w, heads, grid, 0, qk8=qk8)
+    v = patch_scatter(head(x, model_w["hd_w"], model_w["hd_b"]), F, H, W)
+    dt_frame = np.repeat(f64(dts), group)[None, None, :, None, None]
+    z = window + dt_frame * v
+    out = z[:, :, :group]
+    new = np.concatenate([z[:, :, group:], f64(noise_in)], axis=2)
+    return new, out

@@ -698,3 +698,51 @@ def test_fp8_block_reduces_to_the_exact_block_on_representable_weights_and_switc
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
     m[:, 5] = 0.0
     np.testing.assert_array_equal(O.dit_block(x, m, ctx, ww, cfg.heads, cfg.grid, fp8=True), x)
+
+
+# ----------------------------------------------------------------------------- streaming queue
+def test_per_token_modulation_equals_shared_when_uniform_and_splits_by_frame():
+    """A per-token modulation that repeats one (6, D) vector equals the shared form.  When the
+    frames' vectors differ only in the row-local parts (gate1, and the FFN's shift, scale and gate)
+    the result splits by frame: each frame's rows equal the block run with that frame's vector."""
+    from video_diffusion_transformer_forward_amd import synth as S
+    cfg = S.get_config("toy").with_(frames=2, height=4, width=4)
+    w = S.block_weights(cfg, 0)
+    x = S.block_inputs(cfg)
+    ctx = S.context(cfg, "cond")
+    mods = S.modulation(cfg.with_(batch=2))                    # two different (6, D)
+    mods[1, :2] = mods[0, :2]                                  # same shift1 / scale1: same keys and values
+    L = cfg.seq_len
+    per = L // cfg.frames
+    shared = O.dit_block(x, mods[0], ctx, w, cfg.heads, cfg.grid)
+    tok = np.broadcast_to(mods[0], (1, L, 6, cfg.dim))
+    np.testing.assert_allclose(O.dit_block(x, tok, ctx, w, cfg.heads, cfg.grid), shared, rtol=1e-13, atol=1e-13)
+    tok = np.concatenate([np.broadcast_to(mods[f], (1, per, 6, cfg.dim)) for f in range(2)], axis=1)
+    got = O.dit_block(x, tok, ctx, w, cfg.heads, cfg.grid)
+    for f in range(2):
+        rows = list(range(f * per, (f + 1) * per))
+        ref = O.dit_block(x, mods[f], ctx, w, cfg.heads, cfg.grid, rows=rows)
+        np.testing.assert_allclose(got[:, rows], ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(O.dit_block(x, tok, ctx, w, cfg.heads, cfg.grid, rows=rows), ref,
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_stream_tick_shifts_the_queue_and_matches_the_step_when_levels_agree():
+    """With every slot at the same level and step the tick is the guidance-free denoise step of
+    the window (guide 1), whose first slot leaves and whose tail is the new noise."""
+    from video_diffusion_transformer_forward_amd import synth as S
+    cfg = S.get_config("toy_step").with_(frames=4, height=8, width=8, n_blocks=2)
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    z = S.latent(cfg)
+    ctx = S.context(cfg, "cond")
+    noise = np.random.default_rng(3).standard_normal((1, 16, 1, 8, 8))
+    new, out = O.stream_tick(z, ctx, mw, bw, cfg.heads, [400.0] * 4, [0.25] * 4, 1, noise)
+    step = O.denoise_step(z, None, ctx, ctx, mw, bw, cfg.heads, 400.0, 0.25, 1.0)
+    np.testing.assert_allclose(out, step[:, :, :1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(new[:, :, :3], step[:, :, 1:], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(new[:, :, 3:], noise)
+    # zero steps: the queue only shifts
+    new0, out0 = O.stream_tick(z, ctx, mw, bw, cfg.heads, [900.0, 600.0, 300.0, 0.0], [0.0] * 4, 1, noise)
+    np.testing.assert_array_equal(out0, z[:, :, :1])
+    np.testing.assert_array_equal(new0[:, :, :3], z[:, :, 1:])
