@@ -239,6 +239,25 @@ int wan_denoise_step_cached(const wan_shape* s, const wan_model_weights* w, floa
  * the launch count of one class since the last reset, and with reset != 0
  * clears that class.  Enabling adds two event records per launch.
  */
+/* Streaming denoise queue ([P1] 6.2 Streamer: a sliding temporal window
+ * generates videos of any length; 6.3: a distilled consistency model folds the
+ * guidance into the model and needs four sampling steps per frame).  Reading
+ * taken: the latent window (1, 16, frames, height, width) holds K = frames / group
+ * slots of `group` latent frames, slot 0 the oldest.  One tick runs the DiT once
+ * over the whole window with the conditional context only (no guidance), every
+ * token modulated with its slot's time modulation at timestep taus[k]; each
+ * slot's frames then take an Euler step of dts[k] along the predicted
+ * velocity.  The first slot's updated frames are written to frames_out
+ * (1, 16, group, height, width); the window shifts down by one slot (in place)
+ * and noise_in (1, 16, group, height, width) becomes its newest slot.
+ * taus and dts are HOST arrays of K floats.  Shape: batch 1, in_ch 16,
+ * img_len 0, 1 <= K <= 64; mode WAN_BF16, WAN_FP32 or WAN_BF16_QK8
+ * (WAN_E_MODE for WAN_FP8).  RoPE positions are window positions. */
+size_t wan_stream_workspace_bytes(const wan_shape* s, int group, int* status);
+int wan_stream_tick(const wan_shape* s, const wan_model_weights* w, float* window, const void* ctx, const float* taus,
+                    const float* dts, int group, const float* noise_in, float* frames_out, void* ws, size_t ws_bytes,
+                    void* stream);
+
 #define WAN_KERNEL_SELF_ATTENTION 0
 #define WAN_KERNEL_CROSS_ATTENTION 1
 #define WAN_KERNEL_GEMM 2

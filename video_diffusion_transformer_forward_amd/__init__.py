@@ -16,7 +16,8 @@ from .synth import WanConfig
 __all__ = ["shape_of", "DeviceBlock", "DeviceModel", "workspace", "workspace_bytes", "patchify", "time_embed",
            "cache_bytes", "diffusion_cache", "denoise_step_cached",
            "dit_block_forward", "head", "denoise_step", "timing_enable", "timing_read", "WanError",
-           "vae_shape_of", "vae_param_table", "VaeDevice", "vae_workspace", "vae_cache", "vae_decode"]
+           "vae_shape_of", "vae_param_table", "VaeDevice", "vae_workspace", "vae_cache", "vae_decode",
+           "stream_workspace", "stream_tick"]
 
 
 def _torch():
@@ -260,3 +261,25 @@ def vae_decode(sh: N.WanVaeShape, dev: VaeDevice, z, t0: int, n: int, cache, vid
     lib = N.load()
     N.check(lib.wan_vae_decode(ctypes.byref(sh), _ptr(dev.weights), _ptr(dev.fparams), _ptr(z), int(t0), int(n),
                                _ptr(cache), cache.numel(), _ptr(video), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- streaming queue
+def stream_workspace(cfg, group: int, device="cuda"):
+    torch = _torch()
+    st = ctypes.c_int(0)
+    sh = shape_of(cfg)
+    n = N.load().wan_stream_workspace_bytes(ctypes.byref(sh), int(group), ctypes.byref(st))
+    N.check(st.value)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def stream_tick(cfg, model: DeviceModel, window, ctx, taus, dts, group: int, noise_in, frames_out, ws, stream=None):
+    """wan_stream_tick: one tick of the streaming denoise queue (window updated in place)."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    k = len(taus)
+    ta = (ctypes.c_float * k)(*[float(t) for t in taus])
+    da = (ctypes.c_float * k)(*[float(t) for t in dts])
+    N.check(lib.wan_stream_tick(ctypes.byref(sh), ctypes.byref(model.struct), _ptr(window), _ptr(ctx),
+                                ctypes.cast(ta, ctypes.c_void_p), ctypes.cast(da, ctypes.c_void_p), int(group),
+                                _ptr(noise_in), _ptr(frames_out), _ptr(ws), ws.numel(), _stream(stream)))

@@ -30,6 +30,7 @@ ENTRY_HEAD = 4
 EXPORTS = ("wan_status_str", "wan_workspace_bytes", "wan_patchify", "wan_time_embed",
            "wan_dit_block_forward", "wan_head", "wan_denoise_step", "wan_cache_bytes",
            "wan_denoise_step_cached", "wan_timing_enable", "wan_timing_read",
+           "wan_stream_workspace_bytes", "wan_stream_tick",
            "wan_vae_param_count", "wan_vae_param_info", "wan_vae_blob_elems", "wan_vae_workspace_bytes",
            "wan_vae_cache_bytes", "wan_vae_decode")
 
@@ -121,6 +122,11 @@ def load(path: str = LIB_PATH):
     lib.wan_timing_read.restype = ctypes.c_int
     lib.wan_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_longlong), ctypes.c_int]
+    lib.wan_stream_workspace_bytes.restype = ctypes.c_size_t
+    lib.wan_stream_workspace_bytes.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.wan_stream_tick.restype = ctypes.c_int
+    lib.wan_stream_tick.argtypes = [sp, ctypes.POINTER(WanModelWeights), _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
+                                    _vp, ctypes.c_size_t, _vp]
     vs = ctypes.POINTER(WanVaeShape)
     ip = ctypes.POINTER(ctypes.c_int)
     lib.wan_vae_param_count.restype = ctypes.c_int

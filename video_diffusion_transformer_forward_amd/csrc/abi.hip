@@ -317,8 +317,10 @@ enum AttnMode { ATTN_COMPUTE = 0, ATTN_STORE = 1, ATTN_REUSE = 2 };
 template <typename T>
 int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const float* mod, long long mbs,
               const void* ctx, void* ws, const BlockPlan& p, bool rope_ready, hipStream_t st,
-              int attn_mode = ATTN_COMPUTE, void* attn_io = nullptr) {
+              int attn_mode = ATTN_COMPUTE, void* attn_io = nullptr, int lm = 0) {
   const int M = Bb * d.L;
+  // tokens per modulation vector: a batch item's tokens, or (streaming queue) one slot's tokens
+  if (lm <= 0) lm = d.L;
   T* m = reinterpret_cast<T*>(at(ws, p.m));
   T* o = reinterpret_cast<T*>(at(ws, p.o));
   float2* rope = reinterpret_cast<float2*>(at(ws, p.rope));
@@ -352,7 +354,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
       return timed(WAN_KERNEL_ELEMENTWISE, st, [&] {
         return launch_ln_mod8(x, m8, msc, rows_p, P, M, d.D, d.L, shift, scale, shift ? mbs : 0, st);
       });
-    return timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, d.L, shift, scale, shift ? mbs : 0, st); });
+    return timed(WAN_KERNEL_ELEMENTWISE, st, [&] { return launch_ln_mod<T>(x, m, M, d.D, lm, shift, scale, shift ? mbs : 0, st); });
   };
   // A operand of a projection whose input is the LayerNorm output
   auto ln_operand = [&](GemmArgs& g, size_t w8_off, size_t ws_off) {
@@ -404,7 +406,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     g.M = M; g.N = d.D; g.K = d.D;
     g.A = a_out; g.lda = d.D; g.a_rpb = M;
     g.Wt = w->o_w; g.ldw = d.D; g.bias = w->o_b;
-    g.c_rpb = d.L; g.x = x; g.ldx = d.D; g.gate = mod + 2 * d.D; g.gate_bstride = mbs;
+    g.c_rpb = lm; g.x = x; g.ldx = d.D; g.gate = mod + 2 * d.D; g.gate_bstride = mbs;
     HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_RESID, st); }));
   }
 
@@ -502,7 +504,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     g.M = M; g.N = d.D; g.K = d.Ff;
     g.A = hbuf; g.lda = d.Ff; g.a_rpb = M;
     g.Wt = w->ff2_w; g.ldw = d.Ff; g.bias = w->ff2_b;
-    g.c_rpb = d.L; g.x = x; g.ldx = d.D; g.gate = mod + 5 * d.D; g.gate_bstride = mbs;
+    g.c_rpb = lm; g.x = x; g.ldx = d.D; g.gate = mod + 5 * d.D; g.gate_bstride = mbs;
     HIP_TRY(timed(WAN_KERNEL_GEMM, st, [&] { return launch_gemm<T>(g, LOAD_PLAIN, EPI_RESID, st); }));
   }
   return WAN_OK;
@@ -540,6 +542,60 @@ int run_head(const Dims& d, int Bb, const wan_model_weights* w, const float* x, 
   return WAN_OK;
 }
 
+
+// ======================================================================= streaming queue
+struct StreamPlan {
+  size_t x, mod, t1, t2, p, nz;
+  BlockPlan blk;
+  size_t total;
+};
+
+StreamPlan plan_stream(const Dims& d, int K) {
+  StreamPlan p;
+  size_t off = 0;
+  p.x = off;
+  off += al((size_t)d.L * d.D * 4);
+  p.mod = off;
+  off += al((size_t)K * 6 * d.D * 4);
+  p.t1 = off;
+  off += al((size_t)d.D * 4);
+  p.t2 = off;
+  off += al((size_t)d.D * 4);
+  p.p = off;
+  off += al((size_t)d.L * 64 * 4);
+  p.nz = off;
+  off += al((size_t)16 * d.F * d.H * d.W * 4);
+  p.blk = plan_block(d, 1, off);
+  p.total = p.blk.total;
+  return p;
+}
+
+template <typename T>
+int run_stream(const Dims& d, const wan_model_weights* w, float* window, const void* ctx, const float* taus,
+               const float* dts, int K, int group, const float* noise, float* out, void* ws, const StreamPlan& p,
+               hipStream_t st) {
+  float* x = reinterpret_cast<float*>(at(ws, p.x));
+  float* mod = reinterpret_cast<float*>(at(ws, p.mod));
+  float* pbuf = reinterpret_cast<float*>(at(ws, p.p));
+  int rc;
+  for (int k = 0; k < K; ++k)
+    if ((rc = run_time<T>(d, w, taus[k], mod + (size_t)k * 6 * d.D, reinterpret_cast<float*>(at(ws, p.t1)),
+                          reinterpret_cast<float*>(at(ws, p.t2)), st)))
+      return rc;
+  if ((rc = run_patchify<T>(d, 1, window, nullptr, w->pe_w, w->pe_b, x, st))) return rc;
+  const int lm = group * d.Hh * d.Ww;  // tokens of one slot
+  for (int i = 0; i < w->n_blocks; ++i)
+    if ((rc = run_block<T>(d, 1, &w->blocks[i], x, mod, 6LL * d.D, ctx, ws, p.blk, i > 0, st, ATTN_COMPUTE, nullptr,
+                           lm)))
+      return rc;
+  if ((rc = run_head<T>(d, 1, w, x, at(ws, p.blk.m), pbuf, st))) return rc;
+  float* nz = reinterpret_cast<float*>(at(ws, p.nz));
+  HIP_TRY(timed(WAN_KERNEL_ELEMENTWISE, st, [&] {
+    return launch_stream_update(pbuf, window, noise, nz, out, 16, d.F, d.H, d.W, group, dts, K, st);
+  }));
+  HIP_TRY(copy_async(window, nz, (size_t)16 * d.F * d.H * d.W * 4, st));
+  return WAN_OK;
+}
 
 // ======================================================================= Wan-VAE decoder
 // Layer list, parameter table, workspace plan and the launch sequence.
@@ -1051,6 +1107,39 @@ int wan_denoise_step_cached(const wan_shape* s, const wan_model_weights* w, floa
   if (!cache) return WAN_E_NULL;
   return step_entry(s, w, z, cond, ctx_cond, ctx_null, timestep, dt, guide_scale, cache_mode, cache, cache_bytes_,
                     ws, ws_bytes, stream);
+}
+
+size_t wan_stream_workspace_bytes(const wan_shape* s, int group, int* status) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc == WAN_OK && (d.B != 1 || d.Cin != 16 || d.Li != 0 || d.fp8 || group < 1 || d.F % group != 0 ||
+                       d.F / group > STREAM_MAX_SLOTS))
+    rc = WAN_E_SHAPE;
+  if (status) *status = rc;
+  return rc == WAN_OK ? plan_stream(d, d.F / group).total : 0;
+}
+
+int wan_stream_tick(const wan_shape* s, const wan_model_weights* w, float* window, const void* ctx, const float* taus,
+                    const float* dts, int group, const float* noise_in, float* frames_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if (d.fp8) return WAN_E_MODE;
+  if (d.B != 1 || d.Cin != 16 || d.Li != 0 || group < 1 || d.F % group != 0 || d.F / group > STREAM_MAX_SLOTS)
+    return WAN_E_SHAPE;
+  const int K = d.F / group;
+  if (!taus || !dts) return WAN_E_NULL;
+  for (int k = 0; k < K; ++k)
+    if (!isfinite(taus[k]) || !isfinite(dts[k])) return WAN_E_SHAPE;
+  if ((rc = check_model_weights(w, d, true))) return rc;
+  if ((rc = check_ptrs({window, ctx, noise_in, frames_out}))) return rc;
+  const StreamPlan p = plan_stream(d, K);
+  if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return d.mode == WAN_BF16 ? run_stream<bf16>(d, w, window, ctx, taus, dts, K, group, noise_in, frames_out, ws, p, st)
+                            : run_stream<float>(d, w, window, ctx, taus, dts, K, group, noise_in, frames_out, ws, p, st);
 }
 
 int wan_vae_param_count(const wan_vae_shape* s, int* status) {

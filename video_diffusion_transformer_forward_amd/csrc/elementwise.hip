@@ -307,6 +307,38 @@ __global__ void unpatch_kernel(const float* __restrict__ p, const float* __restr
   }
 }
 
+// Streaming queue update of one video window z (C, F, H, W): every frame moves by
+// its slot's step along the head velocity p (rows = tokens, as unpatch_kernel);
+// the first `group` frames go to `out`, the others shift down by `group` into
+// `nz`, whose last `group` frames are the new noise frames.
+struct StreamDts {
+  float v[STREAM_MAX_SLOTS];
+};
+__global__ void stream_update_kernel(const float* __restrict__ p, const float* __restrict__ z,
+                                     const float* __restrict__ noise, float* __restrict__ nz, float* __restrict__ out,
+                                     int C, int F, int H, int W, int group, StreamDts dts) {
+  const long long n = (long long)C * F * H * W;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  long long r = idx;
+  const int xw = (int)(r % W); r /= W;
+  const int yh = (int)(r % H); r /= H;
+  const int f = (int)(r % F); r /= F;
+  const int c = (int)r;
+  const int Hh = H / 2, Ww = W / 2;
+  const long long tok = ((long long)f * Hh + yh / 2) * Ww + xw / 2;
+  const float v = p[tok * (C * 4) + c * 4 + (yh & 1) * 2 + (xw & 1)];
+  const float zn = z[idx] + dts.v[f / group] * v;
+  const long long plane = (long long)H * W;
+  const long long in_frame = (long long)yh * W + xw;
+  if (f < group) {
+    out[((long long)c * group + f) * plane + in_frame] = zn;
+    nz[((long long)c * F + (F - group + f)) * plane + in_frame] = noise[((long long)c * group + f) * plane + in_frame];
+  } else {
+    nz[((long long)c * F + (f - group)) * plane + in_frame] = zn;
+  }
+}
+
 // W [N][K] bf16 -> e4m3 bytes [N][K] plus one scale byte per (row, 128-block) at
 // sc[blk * N + n]; one wave per block, two elements per lane
 __global__ __launch_bounds__(256) void quant_w_kernel(const bf16* __restrict__ W, unsigned char* __restrict__ W8,
@@ -426,6 +458,18 @@ hipError_t launch_unpatch(const float* p, float* out, int B, int C, int F, int H
   if (!p_null) p_null = p + (long long)B * L * C * 4;
   hipLaunchKernelGGL(unpatch_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, p_null, out, B, C, F,
                      H, W, step, dt, guide);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_update(const float* p, const float* z, const float* noise, float* nz, float* out, int C,
+                                int F, int H, int W, int group, const float* dts, int K, hipStream_t st) {
+  const long long n = (long long)C * F * H * W;
+  if (n <= 0) return hipSuccess;
+  if (K < 1 || K > STREAM_MAX_SLOTS || group < 1 || F != K * group) return hipErrorInvalidValue;
+  StreamDts d;
+  for (int k = 0; k < STREAM_MAX_SLOTS; ++k) d.v[k] = k < K ? dts[k] : 0.f;
+  hipLaunchKernelGGL(stream_update_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, z, noise, nz, out,
+                     C, F, H, W, group, d);
   return hipGetLastError();
 }
 

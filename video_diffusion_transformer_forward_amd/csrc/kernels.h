@@ -151,6 +151,13 @@ hipError_t launch_vae_border(void* buf, int frames, int Hp, int Wp, int Cs, hipS
 hipError_t launch_vae_pad_weight(const void* W, const float* b, void* Wp, float* bp, int Cout, int N, int taps, int Cin,
                                  int Cink, hipStream_t st);
 
+// Streaming denoise queue: z (C, F = K * group, H, W) += dts[f / group] * v (v from the head
+// rows p); frames [0, group) -> out (C, group, H, W); the rest shifted down by group into nz,
+// whose last group frames are `noise`.  dts is a host array of K <= STREAM_MAX_SLOTS values.
+constexpr int STREAM_MAX_SLOTS = 64;
+hipError_t launch_stream_update(const float* p, const float* z, const float* noise, float* nz, float* out, int C,
+                                int F, int H, int W, int group, const float* dts, int K, hipStream_t st);
+
 // copy helper (device to device, on the stream)
 hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t st);
 
