@@ -151,6 +151,59 @@ def time_vae(name: str = "vae_480p", reps: int = 3) -> dict:
     return out
 
 
+def time_stream(cfg, model, ctx, slots: int = 4, group: int = 1, ticks: int = 10) -> dict:
+    """Streaming queue at the 1.3B 480p shape: a window of `slots` x `group` latent frames
+    (60 x 104), one tick = one guidance-free DiT pass over the window + the queue update, then
+    the emitted latent frames decoded by the VAE through its feature cache (4 video frames each)."""
+    import torch
+    import numpy as np
+    import video_diffusion_transformer_forward_amd as W
+    from video_diffusion_transformer_forward_amd import vae_synth as VS
+    scfg = cfg.with_(frames=slots * group, batch=1)
+    taus = [1000.0 * (1.0 - (slots - 1 - k) / slots) for k in range(slots)]
+    dts = [1.0 / slots] * slots
+    ws = W.stream_workspace(scfg, group)
+    win = torch.from_numpy(S.latent(scfg)).cuda()
+    noise = torch.from_numpy(np.random.default_rng(0).standard_normal(
+        (1, 16, group, scfg.height, scfg.width)).astype(np.float32)).cuda()
+    out = torch.empty_like(noise)
+    vcfg = VS.get_vae_config("vae_480p")
+    vsh = W.vae_shape_of(vcfg, group)
+    vdev = W.VaeDevice(vsh, VS.vae_params(vcfg))
+    vws = W.vae_workspace(vsh)
+    vcache = W.vae_cache(vsh)
+    video = torch.empty((3, 4 * group, vcfg.out_height, vcfg.out_width), dtype=torch.float32, device="cuda")
+    first = torch.empty((3, 4 * group - 3, vcfg.out_height, vcfg.out_width), dtype=torch.float32, device="cuda")
+
+    def tick(i, decode):
+        W.stream_tick(scfg, model, win, ctx, taus, dts, group, noise, out, ws)
+        if decode:
+            t0 = i * group
+            W.vae_decode(vsh, vdev, out[0], t0, group, vcache, first if t0 == 0 else video, vws)
+
+    tick(0, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(1, ticks + 1):
+        tick(i, False)
+    torch.cuda.synchronize()
+    ms_tick = (time.perf_counter() - t1) / ticks * 1e3
+    t1 = time.perf_counter()
+    for i in range(1, ticks + 1):
+        tick(i, True)
+    torch.cuda.synchronize()
+    ms_both = (time.perf_counter() - t1) / ticks * 1e3
+    assert bool(torch.isfinite(win).all()) and bool(torch.isfinite(video).all())
+    del ws, vws, vcache
+    torch.cuda.empty_cache()
+    return {"workload": f"1.3B DiT, window of {slots} slots x {group} latent frame(s) at 60x104 "
+                        f"(L={slots * group * 1560}), one guidance-free pass per tick; VAE decode of the emitted "
+                        f"frame(s) through the feature cache",
+            "ms_per_tick_dit": round(ms_tick, 2), "ms_per_tick_with_vae": round(ms_both, 2),
+            "video_frames_per_tick": 4 * group,
+            "video_fps": round(4 * group / (ms_both * 1e-3), 1)}
+
+
 def attn_traffic_bytes():
     """Counted bytes per self-attention launch, or None once its sources differ from the measured ones."""
     import hashlib
@@ -396,6 +449,8 @@ def main():
     if not args.no_vae:
         print("[bench] vae decode", file=sys.stderr, flush=True)
         out["vae_decode"] = time_vae()
+        print("[bench] streaming queue", file=sys.stderr, flush=True)
+        out["stream"] = time_stream(cfg, model, ctx_c)
     if args.block_configs:
         out["blocks"] = {}
         for name in [c for c in args.block_configs.split(",") if c]:
