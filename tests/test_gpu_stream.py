@@ -86,3 +86,15 @@ def test_stream_several_ticks(case):
         print(f"{case} tick {i}: emitted {err:.3e}")
         assert err <= tol
     assert rel_err(win, w_ref) <= tol
+
+
+def test_stream_full_shape_one_block():
+    """The bench's streaming shape (480p latent 60 x 104, 4 slots of one frame, L = 6240, 1.3B widths)
+    with one block: one tick against the oracle's tick."""
+    cfg = S.get_config("wan13b_step").with_(frames=4, n_blocks=1, batch=1)
+    announce("stream full shape one block")
+    z0, got, win, ref, w_ref = _run(cfg, 1, 1)
+    e_out = inc_err(got[0], ref[0], z0[:, :, :1])
+    e_win = inc_err(win[:, :, :-1], w_ref[:, :, :-1], z0[:, :, 1:])
+    print(f"full shape: emitted {e_out:.3e}, window {e_win:.3e}")
+    assert e_out <= TOL["bf16"] and e_win <= TOL["bf16"]
