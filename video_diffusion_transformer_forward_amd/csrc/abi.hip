@@ -626,7 +626,10 @@ int vae_check(const wan_vae_shape* s, VaeDims* d) {
   return WAN_OK;
 }
 
-int vcs(int c) { return (c + 63) / 64 * 64; }  // channel stride of a buffer holding c channels
+// channel stride of a buffer holding c channels, and the GEMM width of a convolution
+// producing them: c itself when a tile width divides it (multiples of 64 or 96), else
+// c rounded up to 64 (zero weights in the padding)
+int vcs(int c) { return (c % 64 == 0 || c % 96 == 0) ? c : (c + 63) / 64 * 64; }
 
 struct VaeConvInfo {
   int cout, kt, kh, kw, cin;

@@ -54,7 +54,7 @@ struct Gemm {
   static constexpr size_t LDS_BYTES = PIPE_BYTES > SLAB_MAX ? PIPE_BYTES : SLAB_MAX;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(BN % SW == 0 && SW % 8 == 0, "slab");
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(NW == 4 || NW == 8 || NW == 6, "4, 6 or 8 waves");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(NA * RPD * NW == BM && NB * RPD * NW == BN, "DMA split");
   static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
@@ -816,6 +816,8 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
         // 192-wide outputs: 128x192 tiles of 4 waves (64x96 each), two workgroups per CU
         if (g.N % 192 == 0) return launch_cfg<T, 128, 192, 2, 2, 4, 64, 2, LOAD_CONV, EPI_CONV>(g, st);
         if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOAD_CONV, EPI_CONV>(g, st);
+        // 96-wide outputs: 192x96 tiles of 6 waves (32x96 each), two workgroups per CU
+        if (g.N % 96 == 0) return launch_cfg<T, 192, 96, 6, 1, 4, 64, 2, LOAD_CONV, EPI_CONV>(g, st);
       } else if (epi == EPI_CONV_VIDEO) {
         if (g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOAD_CONV, EPI_CONV_VIDEO>(g, st);
       }
