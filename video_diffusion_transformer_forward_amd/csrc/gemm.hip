@@ -33,7 +33,11 @@ struct Gemm {
   static constexpr int STAGE = (BM + BN) * CPR;  // chunks per stage
   // e4m3: per stage, the scale bytes of the tile's A and W rows (64 rows per wave, 256-byte slots)
   static constexpr int SC_STAGE = F8 ? 256 * WM * WN : 0;
-  static constexpr size_t DATA_BYTES = (size_t)NST * STAGE * sizeof(Chunk<T>);
+  // 128-byte rows of bf16 operands (64-deep k-tiles) use split rings: NST A
+  // stages and two W stages; otherwise one ring of NST (A, W) stages
+  static constexpr bool SPLIT = RB == 128 && LOADER == LOAD_PLAIN && sizeof(T) == 2;
+  static constexpr size_t DATA_BYTES =
+      SPLIT ? (size_t)NST * BM * RB + 2 * (size_t)BN * RB : (size_t)NST * STAGE * sizeof(Chunk<T>);
   static constexpr size_t PIPE_BYTES = DATA_BYTES + (size_t)NST * SC_STAGE;
   // DMA instructions per wave per k-tile: each covers RPD rows
   static constexpr int NW = WM * WN;                   // waves per workgroup
@@ -136,7 +140,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS-DMA targets stay scalar
   const int g2 = lane >> 5;  // lane group: which 8-chunk of a 16-wide k step
   const int l32 = lane & 31;
 
@@ -292,6 +296,132 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       wait_vmcnt<INFLIGHT>();  // k-tile kt+1 (and its scales) have landed
       barrier_lds();
       load_frags8((kt + 1) % NST);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  } else if constexpr (C::SPLIT) {
+    // ---- split LDS-DMA rings, 128-byte rows.  An LDS-DMA instruction over 64-byte
+    // row pieces moves about half the bytes per cycle of one over 128-byte pieces,
+    // so the k-tile is 64 deep; a 256x256 tile then needs 64 KB per stage, and the
+    // 160 KB of LDS hold NST = 3 A stages (32 KB each) and 2 W stages.  At the top
+    // of tile kt the W slice of tile kt+1 goes out first, then the A slice of tile
+    // kt+2, spread over the tile's MFMA slots; the end of the tile waits until
+    // only that A slice may still be in flight.  The copies are buffer loads: one
+    // descriptor per operand based at the tile's first row, 32-bit lane offsets,
+    // and the k offset as the scalar offset, so the refill costs no vector ALU.
+    // The tile runs as KS k steps of TM*TN slots, one MFMA each, closed by a
+    // scheduling barrier: a step reads the fragments of the next step in its first
+    // TM+TN slots; the last step waits and synchronises after SYNC_SLOT MFMAs and
+    // then reads the next tile's first fragments.
+    constexpr int NA = C::NA, NB = C::NB, DPT = NA + NB, RPD = C::RPD, PPR = C::PPR;
+    constexpr int NM = TM * TN, NR = TM + TN;
+    constexpr int SYNC_SLOT = NM > 6 ? 5 : NM - 1;
+    constexpr int A_SB = BM * RB, B_SB = BN * RB;  // stage bytes
+    static_assert(KS % 2 == 0 && NST >= 3, "split rings: even k steps, 3+ A stages");
+    static_assert(((KS - 1) * NM + SYNC_SLOT) * DPT >= (DPT - 1) * KS * NM + 1, "refill issued before the wait");
+    const int pp = lane % PPR;
+    const int rlow = lane / PPR;
+    const T* a_tile;
+    {
+      const int bb = m0 / g.a_rpb;
+      int t = m0 - bb * g.a_rpb;
+      if (g.a_valid > 0) t = min(t, g.a_valid - 1);
+      a_tile = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda;
+    }
+    const T* w_tile = reinterpret_cast<const T*>(g.Wt) + (long long)n0 * g.ldw;
+    unsigned a_vo[NA], b_vo[NB];  // byte offsets from the tile's first row (the host bounds them below 2^32)
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int rt = (wave * NA + i) * RPD + rlow;
+      const int r = min(m0 + rt, g.M - 1);
+      const int bb = r / g.a_rpb;
+      int t = r - bb * g.a_rpb;
+      if (g.a_valid > 0) t = min(t, g.a_valid - 1);
+      const T* src = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda +
+                     swz<RB, CPR>(rt, pp) * 8;
+      a_vo[i] = (unsigned)((src - a_tile) * (long long)sizeof(T));
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int rt = (wave * NB + i) * RPD + rlow;
+      b_vo[i] = (unsigned)(((long long)rt * g.ldw + swz<RB, CPR>(rt, pp) * 8) * (long long)sizeof(T));
+    }
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)a_tile, (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)w_tile, (short)0, -1, 0x00020000);
+    unsigned char* a_ring = smem_raw;
+    unsigned char* b_ring = smem_raw + NST * A_SB;
+    auto dma_a = [&](int t, int d) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(a_ring + (t % NST) * A_SB + (wave * NA + d) * 1024), 16,
+                                               a_vo[d], t * BK * (int)sizeof(T), 0, 0);
+    };
+    auto dma_b = [&](int t, int d) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(b_ring + (t % 2) * B_SB + (wave * NB + d) * 1024), 16,
+                                               b_vo[d], t * BK * (int)sizeof(T), 0, 0);
+    };
+    // refill piece d of tile kt's iteration (indices clamped at the end: the
+    // redundant copies rewrite a stage with the bytes it already holds)
+    auto refill = [&](int kt, int d) {
+      if (d < NB)
+        dma_b(min(kt + 1, nk - 1), d);
+      else
+        dma_a(min(kt + NST - 1, nk - 1), d - NB);
+    };
+    auto read_one = [&](int t, int ks, int buf, int r) {
+      const int c = 2 * ks + g2;
+      if (r < TM) {
+        const Chunk<T>* sa = reinterpret_cast<const Chunk<T>*>(a_ring + (t % NST) * A_SB);
+        const int row = arow0 + 32 * r + l32;
+        fa[buf][r].load(&sa[row * CPR + swz<RB, CPR>(row, c)]);
+      } else {
+        const Chunk<T>* sb = reinterpret_cast<const Chunk<T>*>(b_ring + (t % 2) * B_SB);
+        const int row = brow0 + 32 * (r - TM) + l32;
+        fb[buf][r - TM].load(&sb[row * CPR + swz<RB, CPR>(row, c)]);
+      }
+    };
+    // prologue: W tile 0, A tiles 0 .. NST-2
+#pragma unroll
+    for (int d = 0; d < NB; ++d) dma_b(0, d);
+#pragma unroll
+    for (int s0 = 0; s0 < NST - 1; ++s0)
+#pragma unroll
+      for (int d = 0; d < NA; ++d) dma_a(min(s0, nk - 1), d);
+    wait_vmcnt<(NST - 2) * NA>();
+    barrier_lds();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int buf = ks & 1;
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          {
+            const int i = q / TN, j = q % TN;
+            mma32(acc[i][j], fb[buf][j], fa[buf][i]);
+          }
+          if (ks + 1 < KS) {
+            if (q < NR) read_one(kt, ks + 1, buf ^ 1, q);
+          } else {
+            if (q == SYNC_SLOT) {
+              wait_vmcnt<NA>();  // W and A of tile kt+1 have landed; A of tile kt+NST-1 may be out
+              barrier_lds();
+            }
+            if (q > SYNC_SLOT && q - SYNC_SLOT - 1 < NR) read_one(kt + 1, 0, buf ^ 1, q - SYNC_SLOT - 1);
+            if (q == NM - 1) {
+#pragma unroll
+              for (int r = NM - SYNC_SLOT - 1; r < NR; ++r) read_one(kt + 1, 0, buf ^ 1, r);
+            }
+          }
+          {
+            // refill piece d at slot d * KS * NM / DPT of the tile
+            const int gs = ks * NM + q;
+#pragma unroll
+            for (int d = 0; d < DPT; ++d)
+              if ((d * KS * NM) / DPT == gs) refill(kt, d);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -770,9 +900,25 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The split-ring path addresses each operand from its tile's first row with
+// 32-bit byte offsets: rows of one tile may span a batch boundary of A.
+template <typename T>
+bool split_offsets_fit(const GemmArgs& g) {
+  const long long a_span = (g.a_rpb < g.M ? g.a_bstride : 0LL) + 256LL * g.lda + g.K;
+  const long long w_span = 256LL * g.ldw + g.K;
+  return g.a_bstride >= 0 && a_span * (long long)sizeof(T) < (1LL << 32) &&
+         w_span * (long long)sizeof(T) < (1LL << 32);
+}
+
 template <typename T, int LOADER, int EPI>
 hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
+    // 256x256 tiles of 8 waves over 64-deep k-tiles in split rings (the
+    // refill moves 128-byte row pieces); the configurations below serve K not a
+    // multiple of 64 and the other loaders.
+    if constexpr (LOADER == LOAD_PLAIN)
+      if (g.N % 256 == 0 && g.K % 64 == 0 && split_offsets_fit<T>(g))
+        return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOADER, EPI>(g, st);
     // Short-K GEMMs with a heavy epilogue (GELU, residual read-modify-write):
     // 256x128 tiles of 4 waves and a three-stage ring (72 KB) give two
     // workgroups per CU, so one workgroup's epilogue overlaps the other's main
@@ -853,6 +999,8 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
       // 8-bit q / k need whole heads of 128 in one 128-column slab: 256x256 tiles only
       if constexpr (sizeof(T) == 2) {
         if (g.N % 256 != 0 || g.hd != 128 || !g.qs || !g.ks) return hipErrorInvalidValue;
+        if (g.K % 64 == 0 && split_offsets_fit<T>(g))
+          return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_PLAIN, EPI_PACK8>(g, st);
         return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_PLAIN, EPI_PACK8>(g, st);
       }
       return hipErrorInvalidValue;
