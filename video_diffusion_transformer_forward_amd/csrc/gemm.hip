@@ -32,10 +32,10 @@ struct Gemm {
   static constexpr int TN = BN / WN / 32;
   static constexpr int STAGE = (BM + BN) * CPR;  // chunks per stage
   // e4m3: per stage, the scale bytes of the tile's A and W rows (64 rows per wave, 256-byte slots)
-  static constexpr int SC_STAGE = F8 ? 256 * WM * WN : 0;
+  static constexpr int SC_STAGE = (F8 && RB == 64) ? 256 * WM * WN : 0;
   // 128-byte rows of bf16 operands (64-deep k-tiles) use split rings: NST A
   // stages and two W stages; otherwise one ring of NST (A, W) stages
-  static constexpr bool SPLIT = RB == 128 && LOADER == LOAD_PLAIN && sizeof(T) == 2;
+  static constexpr bool SPLIT = RB == 128 && ((LOADER == LOAD_PLAIN && sizeof(T) == 2) || F8);
   static constexpr size_t DATA_BYTES =
       SPLIT ? (size_t)NST * BM * RB + 2 * (size_t)BN * RB : (size_t)NST * STAGE * sizeof(Chunk<T>);
   static constexpr size_t PIPE_BYTES = DATA_BYTES + (size_t)NST * SC_STAGE;
@@ -63,8 +63,8 @@ struct Gemm {
   static_assert(NA * RPD * NW == BM && NB * RPD * NW == BN, "DMA split");
   static_assert(RB == 64 || RB == 128, "64- or 128-byte rows");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
-  static_assert(!F8 || (BM == 256 && BN == 256 && WM * WN == 8 && RB == 64 && sizeof(T) == 2),
-                "e4m3 operands: 256x256 tiles of 8 waves, 64-byte k-tiles, bf16 output");
+  static_assert(!F8 || (BM == 256 && BN == 256 && WM * WN == 8 && sizeof(T) == 2),
+                "e4m3 operands: 256x256 tiles of 8 waves, bf16 output");
 };
 
 // Physical chunk position of logical chunk c in tile row r (RB-byte rows).  A
@@ -205,7 +205,146 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       for (int j = 0; j < TN; ++j) mma32(acc[i][j], fb[buf][j], fa[buf][i]);
   };
 
-  if constexpr (LOADER == LOAD_FP8) {
+  if constexpr (LOADER == LOAD_FP8 && RB == 128) {
+    // ---- e4m3 operands in split rings: 128-byte rows = 128-deep k-tiles, one
+    // scale block each, in the ring layout and schedule of the bf16 split path
+    // below (A: NST stages, W: 2, buffer-load refills spread over the tile).
+    // Each k-tile is two scaled 32x32x64 MFMA steps.  The scale bytes of a lane's
+    // rows (A: row operand of scale_b, W: of scale_a) are loaded straight into
+    // registers one tile ahead, ahead of the W refill, so the tile-end wait
+    // covers them.  MFMA row operand = W rows, column operand = A rows.
+    constexpr int NA = C::NA, NB = C::NB, DPT = NA + NB, RPD = C::RPD, PPR = C::PPR;
+    constexpr int NM = TM * TN, NR = TM + TN;
+    constexpr int K8 = BK / 64;  // scaled k steps per tile
+    constexpr int SYNC_SLOT = 1;
+    constexpr int A_SB = BM * RB, B_SB = BN * RB;
+    static_assert(K8 == 2 && NST >= 3 && NM >= NR && SYNC_SLOT <= TM - 1, "e4m3 split rings");
+    const int pp = lane % PPR;
+    const int rlow = lane / PPR;
+    const unsigned char* a_tile;
+    {
+      const int bb = m0 / g.a_rpb;
+      int t = m0 - bb * g.a_rpb;
+      if (g.a_valid > 0) t = min(t, g.a_valid - 1);
+      a_tile = reinterpret_cast<const unsigned char*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda;
+    }
+    const unsigned char* w_tile = reinterpret_cast<const unsigned char*>(g.Wt) + (long long)n0 * g.ldw;
+    unsigned a_vo[NA], b_vo[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int rt = (wave * NA + i) * RPD + rlow;
+      const int r = min(m0 + rt, g.M - 1);
+      const int bb = r / g.a_rpb;
+      int t = r - bb * g.a_rpb;
+      if (g.a_valid > 0) t = min(t, g.a_valid - 1);
+      a_vo[i] = (unsigned)((long long)bb * g.a_bstride + (long long)t * g.lda - (a_tile - reinterpret_cast<const unsigned char*>(g.A)) +
+                           swz<RB, CPR>(rt, pp) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int rt = (wave * NB + i) * RPD + rlow;
+      b_vo[i] = (unsigned)((long long)rt * g.ldw + swz<RB, CPR>(rt, pp) * 16);
+    }
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)a_tile, (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)w_tile, (short)0, -1, 0x00020000);
+    unsigned char* a_ring = smem_raw;
+    unsigned char* b_ring = smem_raw + NST * A_SB;
+    auto dma_a = [&](int t, int d) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(a_ring + (t % NST) * A_SB + (wave * NA + d) * 1024), 16,
+                                               a_vo[d], t * BK, 0, 0);
+    };
+    auto dma_b = [&](int t, int d) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(b_ring + (t % 2) * B_SB + (wave * NB + d) * 1024), 16,
+                                               b_vo[d], t * BK, 0, 0);
+    };
+    auto refill = [&](int kt, int d) {
+      if (d < NB)
+        dma_b(min(kt + 1, nk - 1), d);
+      else
+        dma_a(min(kt + NST - 1, nk - 1), d - NB);
+    };
+    // scale bytes of this lane's rows for k-block t: buffer loads at lane offset
+    // l32 + 32 i from a scalar base (descriptor at the tile's rows, k-block offset scalar)
+    const __amdgpu_buffer_rsrc_t rca = __builtin_amdgcn_make_buffer_rsrc((void*)(g.a_scale + m0 + arow0), (short)0, -1,
+                                                                         0x00020000);
+    const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc((void*)(g.w_scale + n0 + brow0), (short)0, -1,
+                                                                         0x00020000);
+    int sa8[TM], sb8[TN], nsa[TM], nsb[TN];
+    auto load_scales = [&](int t, int (&xa)[TM], int (&xb)[TN]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) xa[i] = __builtin_amdgcn_raw_buffer_load_b8(rca, l32 + 32 * i, t * g.a_sld, 0);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) xb[j] = __builtin_amdgcn_raw_buffer_load_b8(rcb, l32 + 32 * j, t * g.N, 0);
+    };
+    // Fragments are single-buffered: the MFMAs of a step run W-fragment-major,
+    // (i, j) at slot j * TM + i, so W fragment j is dead after slot j * TM + TM - 1
+    // and A fragment i after slot (TN - 1) * TM + i; the next step's copy of each is
+    // read in the slot where it dies.
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    i32x8 fa8[TM], fb8[TN];
+    auto read_frag = [&](int t, int ks, const unsigned char* base, int row) {
+      const int p0 = 4 * ks + 2 * g2;
+      const unsigned char* rowp = base + row * RB;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + swz<RB, CPR>(row, p0) * 16);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(rowp + swz<RB, CPR>(row, p0 + 1) * 16);
+      return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto read_a = [&](int t, int ks, int i) {
+      fa8[i] = read_frag(t, ks, a_ring + (t % NST) * A_SB, arow0 + 32 * i + l32);
+    };
+    auto read_b = [&](int t, int ks, int j) {
+      fb8[j] = read_frag(t, ks, b_ring + (t % 2) * B_SB, brow0 + 32 * j + l32);
+    };
+#pragma unroll
+    for (int d = 0; d < NB; ++d) dma_b(0, d);
+#pragma unroll
+    for (int s0 = 0; s0 < NST - 1; ++s0)
+#pragma unroll
+      for (int d = 0; d < NA; ++d) dma_a(min(s0, nk - 1), d);
+    load_scales(0, sa8, sb8);
+    wait_vmcnt<0>();
+    barrier_lds();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_a(0, 0, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) read_b(0, 0, j);
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int ks = 0; ks < K8; ++ks) {
+        const bool last = ks + 1 == K8;
+        const int tn = last ? kt + 1 : kt;   // tile and step of the fragments read in this step
+        const int kn = last ? 0 : ks + 1;
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          if (ks == 0 && q == 0) load_scales(min(kt + 1, nk - 1), nsa, nsb);
+          const int i = q % TM, j = q / TM;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[j], fa8[i], acc[i][j], 0, 0, 0, sb8[j], 0,
+                                                                      sa8[i]);
+          if (last && q == SYNC_SLOT) {
+            wait_vmcnt<NA>();  // scales, W and A of tile kt+1 have landed
+            barrier_lds();
+          }
+          if (j == TN - 1) read_a(tn, kn, i);  // A fragment i is dead from here
+          if (i == TM - 1) read_b(tn, kn, j);  // W fragment j is dead from here
+          {
+            // refill piece d at slot d * SPAN / DPT: all of them before the tile-end wait
+            constexpr int SPAN = (K8 - 1) * NM + SYNC_SLOT;
+            const int gs = ks * NM + q;
+#pragma unroll
+            for (int d = 0; d < DPT; ++d)
+              if ((d * SPAN) / DPT == gs) refill(kt, d);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa8[i] = nsa[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb8[j] = nsb[j];
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  } else if constexpr (LOADER == LOAD_FP8) {
     // ---- e4m3 operands: the LDS-DMA ring of the bf16 path with 64-byte k-tiles
     // (64 elements, one scaled 32x32x64 MFMA step) plus, per stage, the scale
     // bytes of the tile's 256 A rows (waves 0-3) and 256 W rows (waves 4-7) for
@@ -976,15 +1115,24 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
       if (g.N % 256 != 0 || g.K % 128 != 0 || g.M % 256 != 0 || !g.a_scale || !g.w_scale || g.a_sld < g.M)
         return hipErrorInvalidValue;
+      // split rings of 128-deep k-tiles when the tile-relative byte offsets fit 32 bits
+      const bool split = ((g.a_rpb < g.M ? g.a_bstride : 0LL) + 256LL * g.lda + g.K) < (1LL << 32) &&
+                         (256LL * g.ldw + g.K) < (1LL << 32) && g.a_bstride >= 0;
       switch (epi) {
-        case EPI_PACK: return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_PACK>(g, st);
+        case EPI_PACK:
+          if (split) return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_FP8, EPI_PACK>(g, st);
+          return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_PACK>(g, st);
         case EPI_PACK8:
           if (g.hd != 128 || !g.qs || !g.ks) return hipErrorInvalidValue;
+          if (split) return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_FP8, EPI_PACK8>(g, st);
           return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_PACK8>(g, st);
         case EPI_STORE_GELU8:
           if (!g.c_scale || g.c_sld < g.M) return hipErrorInvalidValue;
+          if (split) return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_FP8, EPI_STORE_GELU8>(g, st);
           return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_STORE_GELU8>(g, st);
-        case EPI_RESID: return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_RESID>(g, st);
+        case EPI_RESID:
+          if (split) return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_FP8, EPI_RESID>(g, st);
+          return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_FP8, EPI_RESID>(g, st);
       }
     }
     return hipErrorInvalidValue;
