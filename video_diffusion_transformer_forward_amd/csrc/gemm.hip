@@ -1041,11 +1041,17 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 
 // The split-ring path addresses each operand from its tile's first row with
 // 32-bit byte offsets: rows of one tile may span a batch boundary of A.
+// Elements from a tile's first A row to the end of its last k-slice: a tile of
+// 256 rows spans at most 256 / a_rpb + 1 batch items.
+inline long long split_a_span(const GemmArgs& g) {
+  const long long items = g.a_rpb < g.M ? 256LL / g.a_rpb + 1 : 0LL;
+  return items * g.a_bstride + 256LL * g.lda + g.K;
+}
+
 template <typename T>
 bool split_offsets_fit(const GemmArgs& g) {
-  const long long a_span = (g.a_rpb < g.M ? g.a_bstride : 0LL) + 256LL * g.lda + g.K;
   const long long w_span = 256LL * g.ldw + g.K;
-  return g.a_bstride >= 0 && a_span * (long long)sizeof(T) < (1LL << 32) &&
+  return g.a_bstride >= 0 && split_a_span(g) * (long long)sizeof(T) < (1LL << 32) &&
          w_span * (long long)sizeof(T) < (1LL << 32);
 }
 
@@ -1116,8 +1122,7 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
       if (g.N % 256 != 0 || g.K % 128 != 0 || g.M % 256 != 0 || !g.a_scale || !g.w_scale || g.a_sld < g.M)
         return hipErrorInvalidValue;
       // split rings of 128-deep k-tiles when the tile-relative byte offsets fit 32 bits
-      const bool split = ((g.a_rpb < g.M ? g.a_bstride : 0LL) + 256LL * g.lda + g.K) < (1LL << 32) &&
-                         (256LL * g.ldw + g.K) < (1LL << 32) && g.a_bstride >= 0;
+      const bool split = split_offsets_fit<unsigned char>(g);  // e4m3: one byte per element
       switch (epi) {
         case EPI_PACK:
           if (split) return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_FP8, EPI_PACK>(g, st);
