@@ -35,7 +35,7 @@ struct Gemm {
   static constexpr int SC_STAGE = (F8 && RB == 64) ? 256 * WM * WN : 0;
   // 128-byte rows of bf16 operands (64-deep k-tiles) use split rings: NST A
   // stages and two W stages; otherwise one ring of NST (A, W) stages
-  static constexpr bool SPLIT = RB == 128 && ((LOADER == LOAD_PLAIN && sizeof(T) == 2) || F8);
+  static constexpr bool SPLIT = RB == 128 && (((LOADER == LOAD_PLAIN || LOADER == LOAD_CONV) && sizeof(T) == 2) || F8);
   static constexpr size_t DATA_BYTES =
       SPLIT ? (size_t)NST * BM * RB + 2 * (size_t)BN * RB : (size_t)NST * STAGE * sizeof(Chunk<T>);
   static constexpr size_t PIPE_BYTES = DATA_BYTES + (size_t)NST * SC_STAGE;
@@ -444,42 +444,63 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     // so the k-tile is 64 deep; a 256x256 tile then needs 64 KB per stage, and the
     // 160 KB of LDS hold NST = 3 A stages (32 KB each) and 2 W stages.  At the top
     // of tile kt the W slice of tile kt+1 goes out first, then the A slice of tile
-    // kt+2, spread over the tile's MFMA slots; the end of the tile waits until
-    // only that A slice may still be in flight.  The copies are buffer loads: one
-    // descriptor per operand based at the tile's first row, 32-bit lane offsets,
-    // and the k offset as the scalar offset, so the refill costs no vector ALU.
+    // kt+2, spread over the MFMA slots before the tile-end wait, which lets only
+    // that A slice stay in flight.  The copies are buffer loads (one descriptor per
+    // operand based at the tile's first row, 32-bit lane offsets, the k offset as
+    // the scalar offset: no vector ALU per refill), except the convolution's A
+    // operand, whose per-tap offsets go onto 64-bit lane addresses.
     // The tile runs as KS k steps of TM*TN slots, one MFMA each, closed by a
     // scheduling barrier: a step reads the fragments of the next step in its first
-    // TM+TN slots; the last step waits and synchronises after SYNC_SLOT MFMAs and
-    // then reads the next tile's first fragments.
+    // TM+TN slots; the last step waits and synchronises after SYNC_SLOT + 1 MFMAs
+    // and then reads the next tile's first fragments.
     constexpr int NA = C::NA, NB = C::NB, DPT = NA + NB, RPD = C::RPD, PPR = C::PPR;
     constexpr int NM = TM * TN, NR = TM + TN;
-    constexpr int SYNC_SLOT = NM > 6 ? 5 : NM - 1;
+    constexpr int SYNC_SLOT = NM - NR - 1 > 0 ? NM - NR - 1 : 0;
+    constexpr int SPAN = (KS - 1) * NM + SYNC_SLOT;  // slots before the wait: the refills go out over them
     constexpr int A_SB = BM * RB, B_SB = BN * RB;  // stage bytes
-    static_assert(KS % 2 == 0 && NST >= 3, "split rings: even k steps, 3+ A stages");
-    static_assert(((KS - 1) * NM + SYNC_SLOT) * DPT >= (DPT - 1) * KS * NM + 1, "refill issued before the wait");
+    static_assert(KS % 2 == 0 && NST >= 3 && NM >= NR, "split rings: even k steps, 3+ A stages");
     const int pp = lane % PPR;
     const int rlow = lane / PPR;
-    const T* a_tile;
-    {
-      const int bb = m0 / g.a_rpb;
-      int t = m0 - bb * g.a_rpb;
-      if (g.a_valid > 0) t = min(t, g.a_valid - 1);
-      a_tile = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda;
+    // A rows: token rows of the plain loader, or output voxels of the convolution
+    // loader (its tap offsets, some negative, are added per k-tile to 64-bit
+    // addresses; a tap's channels span kpt 64-deep k-tiles)
+    const T* a_tile = reinterpret_cast<const T*>(g.A);
+    unsigned a_vo[NA];  // byte offsets from the tile's first row (the host bounds them below 2^32)
+    const T* a_src[LOADER == LOAD_CONV ? NA : 1];
+    const int kpt = LOADER == LOAD_CONV ? g.cv_kpt / 2 : 1;
+    if constexpr (LOADER == LOAD_CONV) {
+      const int hw = g.cv_h * g.cv_w;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int rt = (wave * NA + i) * RPD + rlow;
+        const int r = min(m0 + rt, g.M - 1);
+        const int tv = r / hw, rem = r - tv * hw;
+        const int hv = rem / g.cv_w, wv = rem - hv * g.cv_w;
+        a_src[i] = reinterpret_cast<const T*>(g.A) +
+                   (((long long)(tv + g.cv_t0) * g.cv_hp + hv) * g.cv_wp + wv) * g.lda + swz<RB, CPR>(rt, pp) * 8;
+        a_vo[i] = 0;
+      }
+    } else {
+      {
+        const int bb = m0 / g.a_rpb;
+        int t = m0 - bb * g.a_rpb;
+        if (g.a_valid > 0) t = min(t, g.a_valid - 1);
+        a_tile = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda;
+      }
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int rt = (wave * NA + i) * RPD + rlow;
+        const int r = min(m0 + rt, g.M - 1);
+        const int bb = r / g.a_rpb;
+        int t = r - bb * g.a_rpb;
+        if (g.a_valid > 0) t = min(t, g.a_valid - 1);
+        const T* src = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda +
+                       swz<RB, CPR>(rt, pp) * 8;
+        a_vo[i] = (unsigned)((src - a_tile) * (long long)sizeof(T));
+      }
     }
     const T* w_tile = reinterpret_cast<const T*>(g.Wt) + (long long)n0 * g.ldw;
-    unsigned a_vo[NA], b_vo[NB];  // byte offsets from the tile's first row (the host bounds them below 2^32)
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int rt = (wave * NA + i) * RPD + rlow;
-      const int r = min(m0 + rt, g.M - 1);
-      const int bb = r / g.a_rpb;
-      int t = r - bb * g.a_rpb;
-      if (g.a_valid > 0) t = min(t, g.a_valid - 1);
-      const T* src = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda +
-                     swz<RB, CPR>(rt, pp) * 8;
-      a_vo[i] = (unsigned)((src - a_tile) * (long long)sizeof(T));
-    }
+    unsigned b_vo[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int rt = (wave * NB + i) * RPD + rlow;
@@ -490,8 +511,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     unsigned char* a_ring = smem_raw;
     unsigned char* b_ring = smem_raw + NST * A_SB;
     auto dma_a = [&](int t, int d) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(a_ring + (t % NST) * A_SB + (wave * NA + d) * 1024), 16,
-                                               a_vo[d], t * BK * (int)sizeof(T), 0, 0);
+      lds_void* dst = (lds_void*)(a_ring + (t % NST) * A_SB + (wave * NA + d) * 1024);
+      if constexpr (LOADER == LOAD_CONV) {
+        const int tap = t / kpt;
+        __builtin_amdgcn_global_load_lds(a_src[d] + g.tap_off[tap] + (long long)(t - tap * kpt) * BK, dst, 16, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, a_vo[d], t * BK * (int)sizeof(T), 0, 0);
+      }
     };
     auto dma_b = [&](int t, int d) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(b_ring + (t % 2) * B_SB + (wave * NB + d) * 1024), 16,
@@ -552,11 +578,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             }
           }
           {
-            // refill piece d at slot d * KS * NM / DPT of the tile
+            // refill piece d at slot d * SPAN / DPT, all before the tile-end wait
             const int gs = ks * NM + q;
 #pragma unroll
             for (int d = 0; d < DPT; ++d)
-              if ((d * KS * NM) / DPT == gs) refill(kt, d);
+              if ((d * SPAN) / DPT == gs) refill(kt, d);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1102,6 +1128,11 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
           g.cv_h < 1 || g.cv_w < 1)
         return hipErrorInvalidValue;
       if (epi == EPI_CONV) {
+        // taps of whole 64-channel k-tiles: split rings, 256x256 or 256x192 tiles (64x96 per wave)
+        if (g.cv_kpt % 2 == 0) {
+          if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_CONV, EPI_CONV>(g, st);
+          if (g.N % 192 == 0) return launch_cfg<T, 256, 192, 4, 2, 3, 128, 1, LOAD_CONV, EPI_CONV>(g, st);
+        }
         if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOAD_CONV, EPI_CONV>(g, st);
         if (g.N % 128 == 0) return launch_cfg<T, 256, 128, 2, 2, 3, 64, 2, LOAD_CONV, EPI_CONV>(g, st);
         // 192-wide outputs: 128x192 tiles of 4 waves (64x96 each), two workgroups per CU
