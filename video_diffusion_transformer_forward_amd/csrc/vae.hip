@@ -71,11 +71,13 @@ __global__ __launch_bounds__(256) void vae_rms_silu_kernel(const bf16* __restric
     const float4 g0 = *reinterpret_cast<const float4*>(g + c0);
     const float4 g1 = *reinterpret_cast<const float4*>(g + c0 + 4);
     const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    // SiLU as r / (1 + 2^(-r log2 e)) with the hardware exp2 and reciprocal (about
+    // 1 ulp each, far below the bf16 rounding of the result); r -> -inf gives -0
     float y[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float r = x[u] * inv * gg[u];
-      y[u] = r / (1.0f + expf(-r));
+      y[u] = r * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(r * -1.4426950408889634f));
     }
     Chunk<bf16> c;
     pack8(c, y);
