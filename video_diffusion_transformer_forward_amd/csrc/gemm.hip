@@ -1,16 +1,24 @@
 // LDS-tiled MFMA GEMM for gfx950: C = A W^T + bias with fused epilogues.
 //
-// WM x WN waves per workgroup (4 or 8) compute a BM x BN tile in BK-deep
+// WM x WN waves per workgroup (4, 6 or 8) compute a BM x BN tile in BK-deep
 // k-tiles.  Operand tiles stream global -> LDS through the 16-byte LDS-DMA
-// path into an NST-stage ring, so the loads of a k-tile are issued NST-1 tiles
-// ahead of its MFMAs; one barrier per k-tile.  Inside a k-tile the MFMA operand
-// fragments are double-buffered in registers, so the LDS reads of one 16-deep
-// k-step overlap the MFMAs of the previous one.  Tile rows are 64 bytes: four
-// 16-byte chunks whose position is XOR-swizzled with row bits 2..3, which puts
-// the 16 rows one wave-wide operand read touches on distinct banks.  Tiles are
-// ordered in groups of 8 M-tiles and the hardware workgroup order is remapped
-// so that each XCD (with its own L2) works through one contiguous range.
-// The epilogue stages the fp32 tile in LDS and writes 16-byte pieces.
+// path, so the loads of a k-tile are issued tiles ahead of its MFMAs; one
+// barrier per k-tile.  Two ring layouts:
+//  - 128-byte tile rows (64-deep bf16 or 128-deep e4m3 k-tiles): split rings,
+//    NST A stages and two W stages, refilled by buffer loads spread over the
+//    MFMA slots of the tile (the bf16 projections, the e4m3 projections and the
+//    convolutions with 64-channel taps);
+//  - 64-byte tile rows: one NST-stage ring of (A, W) stages (fp32 operands, the
+//    patch gather, convolutions with 32- or 96-channel taps).
+// An LDS-DMA instruction moves about twice the bytes per cycle over 128-byte
+// row pieces as over 64-byte ones, which is why the wider rows are preferred.
+// Inside a k-tile the MFMA operand fragments of the next 16-deep step are read
+// while the current step's MFMAs run.  Tile rows hold 16-byte chunks whose
+// position is XOR-swizzled with low row bits, which puts the 16 rows one
+// wave-wide operand read touches on distinct banks.  Tiles are ordered in groups
+// of 8 M-tiles and the hardware workgroup order is remapped so that each XCD
+// (with its own L2) works through one contiguous range.  The epilogue stages
+// the fp32 tile in LDS and writes 16-byte pieces.
 #include "common.h"
 #include "kernels.h"
 
