@@ -1098,12 +1098,12 @@ hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
     if constexpr (LOADER == LOAD_PLAIN)
       if (g.N % 256 == 0 && g.K % 64 == 0 && split_offsets_fit<T>(g))
         return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOADER, EPI>(g, st);
-    // Short-K GEMMs with a heavy epilogue (GELU, residual read-modify-write):
-    // 256x128 tiles of 4 waves and a three-stage ring (72 KB) give two
-    // workgroups per CU, so one workgroup's epilogue overlaps the other's main
-    // loop.  Otherwise 256x256 tiles of 8 waves (two per SIMD, 64x128 each) and
-    // a four-stage ring: one workgroup per CU, the fewest operand bytes per flop,
-    // and a second wave on every SIMD to cover barrier and LDS waits.
+    // Fallbacks on 64-byte rows (K not a multiple of 64, lane offsets beyond 32
+    // bits, N not a multiple of 256).  Short-K GEMMs with a heavy epilogue (GELU,
+    // residual read-modify-write): 256x128 tiles of 4 waves and a three-stage
+    // ring (72 KB) give two workgroups per CU, so one workgroup's epilogue
+    // overlaps the other's main loop.  Otherwise 256x256 tiles of 8 waves (two
+    // per SIMD, 64x128 each) and a four-stage ring, or 128x64 tiles.
     constexpr bool heavy_epi = EPI == EPI_STORE_GELU || EPI == EPI_RESID;
     if (heavy_epi && g.K <= 2048 && g.N % 128 == 0) return launch_cfg<T, 256, 128, 2, 2, 3, 64, 2, LOADER, EPI>(g, st);
     if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, 4, 64, 1, LOADER, EPI>(g, st);
