@@ -1159,7 +1159,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     if constexpr (sizeof(T) == 2) return launch_attn_qk8<2, 8>(a, st);
   }
   if constexpr (sizeof(T) == 2) {
-    if (a.hd == 128 && a.nsrc == 1 && a.self) return launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW>(a, st);
+    if (a.hd == 128 && a.nsrc == 1 && a.self) {
+      // Fewer 256-query workgroups than two rounds of the 256 CUs (short sequences):
+      // 128-query workgroups of 4 waves, two per CU, so the last round runs on
+      // finer pieces (at full length the 8-wave form is about 7% faster).
+      const long long g8 = (long long)((a.Lq + 255) / 256) * a.heads * a.B;
+      if (g8 < 512) return launch_attn_wide<128, WIDE_NR, 1, 4>(a, st);
+      return launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW>(a, st);
+    }
   }
   if (a.hd == 128) {
     if (a.nsrc == 1) return launch_attn_cfg<T, 128, 1>(a, st);
