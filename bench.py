@@ -28,15 +28,15 @@ MI355X_FP32_TFLOPS = 157.3
 CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 
 # L2 <-> memory bytes of one self-attention launch, from two counter-collection runs of
-# `bench.py --steps 1 --warmup 0 --no-cpu-baseline --calib-copy` (FETCH_SIZE, then WRITE_SIZE,
+# `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-cache-modes --no-vae --calib-copy` (FETCH_SIZE, then WRITE_SIZE,
 # KiB per dispatch), each scaled by known/counted bytes of the 1 GiB calibration copy in the
 # same run.  Valid only for the kernel sources they were taken on (checked by hash).
 ATTN_COUNTERS = {
-    "fetch_kib": 884803.06, "fetch_scale": 1048576 / 524306.44,
+    "fetch_kib": 884803.94, "fetch_scale": 1048576 / 524306.33,
     "write_kib": 196560.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "1ea43fde7dbec62c2403aed17295014bb09172677600b523c59ee86900456be5",
+    "sha256": "408ac36191ea87a51627792c2abb3f63087cc2c990e425edd0a2df6e3ddac6da",
 }
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 
