@@ -69,29 +69,97 @@ def step_flops(cfg: S.WanConfig) -> float:
     return cfg.n_blocks * per_block + patch + head + time_mlp
 
 
-def time_block(bcfg: S.WanConfig, reps: int = 5) -> dict:
-    """ms and TFLOP/s of one wan_dit_block_forward on a single video of bcfg's shape (inputs resident)."""
+class ClockSampler:
+    """Samples the current GPU core and memory clock levels (sysfs pp_dpm_sclk / pp_dpm_mclk, the
+    line marked '*') every `period` seconds on a background thread; reads only."""
+
+    def __init__(self, period: float = 0.25):
+        import glob
+        import threading
+        self.files = {}
+        for kind in ("sclk", "mclk"):
+            found = sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}"))
+            if found:
+                self.files[kind] = found[0]
+        self.samples = {k: [] for k in self.files}
+        self.period = period
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self, path):
+        try:
+            with open(path) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k, f in self.files.items():
+                v = self._read(f)
+                if v is not None:
+                    self.samples[k].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.files:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.files:
+            self._thread.join(timeout=2.0)
+
+    def summary(self):
+        out = {}
+        for k, v in self.samples.items():
+            if v:
+                v = sorted(v)
+                out[f"{k}_mhz"] = {"min": v[0], "median": v[len(v) // 2], "max": v[-1], "samples": len(v)}
+        return out or None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_block(bcfg: S.WanConfig, reps: int = 6, n_sets: int = 3) -> dict:
+    """ms and TFLOP/s of one wan_dit_block_forward on a single video of bcfg's shape (inputs resident).
+    The timed calls rotate over n_sets distinct weight sets, so that one block's weights (93 MB at the
+    1.3B shape) are not served from the 256 MB Infinity Cache every time."""
     import torch
     import video_diffusion_transformer_forward_amd as W
     from video_diffusion_transformer_forward_amd import _native as N
-    blk = W.DeviceBlock(bcfg, S.block_weights(bcfg, 0))
+    blks = [W.DeviceBlock(bcfg, S.block_weights(bcfg, b)) for b in range(n_sets)]
     x = torch.from_numpy(S.block_inputs(bcfg)).cuda()
     mod = torch.from_numpy(S.modulation(bcfg)).cuda()
     ctx = torch.from_numpy(S.context(bcfg, "cond")).to(W.elem_dtype(bcfg)).cuda()
     ws = W.workspace(bcfg, N.ENTRY_BLOCK)
-    for _ in range(2):
-        W.dit_block_forward(bcfg, blk, x, mod, ctx, ws)
+    for b in range(n_sets):
+        W.dit_block_forward(bcfg, blks[b], x, mod, ctx, ws)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(reps):
-        W.dit_block_forward(bcfg, blk, x, mod, ctx, ws)
+    for i in range(reps):
+        W.dit_block_forward(bcfg, blks[i % n_sets], x, mod, ctx, ws)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / reps * 1e3
     fl = sum(block_flops(bcfg, bcfg.batch).values())
-    del blk, x, mod, ctx, ws
+    del blks, x, mod, ctx, ws
     torch.cuda.empty_cache()
     return {"ms_per_block": round(ms, 3), "block_tflop": round(fl / 1e12, 3),
-            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "seq_len": bcfg.seq_len, "dim": bcfg.dim}
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "seq_len": bcfg.seq_len, "dim": bcfg.dim,
+            "weight_sets": n_sets}
 
 
 def vae_flops(vcfg) -> float:
@@ -247,6 +315,7 @@ def cpu_baseline(cfg: S.WanConfig, budget_s: float = 20.0) -> dict:
     except Exception:
         threads = os.cpu_count()
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"float64 oracle, one 1.3B block (L=32760, D=1536): k/v of all tokens, outputs of {n} "
                       f"query rows; {fl / 1e12:.3f} TFLOP in {dt:.1f} s",
             "seconds": dt}
@@ -311,12 +380,17 @@ def main():
     for k in range(4):
         W.timing_read(k, reset=True)
     print("[bench] timed steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    with ClockSampler() as clocks:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record()
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     W.timing_enable(False)
     kt = {k: W.timing_read(c) for k, c in (("self_attention", N.KERNEL_SELF_ATTENTION),
                                            ("cross_attention", N.KERNEL_CROSS_ATTENTION),
@@ -403,6 +477,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
+        "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 3), "min": round(step_ms[0], 3),
+                           "max": round(step_ms[-1], 3)},
+        "clocks_during_timed_steps": clocks.summary(),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
