@@ -324,8 +324,8 @@ def cpu_baseline(cfg: S.WanConfig, budget_s: float = 20.0) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="wan13b_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-modes", action="store_true", help="skip timing the diffusion-cache step modes")
