@@ -1095,12 +1095,15 @@ hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
     // 256x256 tiles of 8 waves over 64-deep k-tiles in split rings (the
     // refill moves 128-byte row pieces); the configurations below serve K not a
     // multiple of 64 and the other loaders.
-    // Fewer than 128 such tiles (the context K / V projections) would leave
-    // most CUs idle: 128x64 tiles instead.
+    // Fewer tiles than CUs (short sequences): 256x192 tiles (64x96 per wave) when
+    // N allows, a third more of them; fewer than 128 tiles (the context K / V
+    // projections): 128x64 tiles instead.
     const long long big_tiles = (long long)((g.M + 255) / 256) * (g.N / 256);
     if constexpr (LOADER == LOAD_PLAIN)
-      if (g.N % 256 == 0 && g.K % 64 == 0 && big_tiles >= 128 && split_offsets_fit<T>(g))
+      if (g.N % 256 == 0 && g.K % 64 == 0 && big_tiles >= 128 && split_offsets_fit<T>(g)) {
+        if (big_tiles < 256 && g.N % 192 == 0) return launch_cfg<T, 256, 192, 4, 2, 3, 128, 1, LOADER, EPI>(g, st);
         return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOADER, EPI>(g, st);
+      }
     if constexpr (LOADER == LOAD_PLAIN)
       if (big_tiles < 128 && g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOADER, EPI>(g, st);
     // Fallbacks on 64-byte rows (K not a multiple of 64, lane offsets beyond 32
