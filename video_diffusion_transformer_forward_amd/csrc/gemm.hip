@@ -1144,6 +1144,11 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
           g.cv_h < 1 || g.cv_w < 1)
         return hipErrorInvalidValue;
       if (epi == EPI_CONV) {
+        // a small chunk (fewer than 128 tiles of 256 rows, e.g. one latent frame at the
+        // lowest level): 128x64 tiles, so that most CUs get work
+        const long long rows256 = (g.M + 255) / 256;
+        const long long tiles = rows256 * (g.N % 256 == 0 ? g.N / 256 : g.N % 192 == 0 ? g.N / 192 : g.N / 128);
+        if (tiles < 128 && g.N % 64 == 0) return launch_cfg<T, 128, 64, 4, 1, 4, 64, 1, LOAD_CONV, EPI_CONV>(g, st);
         // taps of whole 64-channel k-tiles: split rings, 256x256 or 256x192 tiles (64x96 per wave)
         if (g.cv_kpt % 2 == 0) {
           if (g.N % 256 == 0) return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOAD_CONV, EPI_CONV>(g, st);
