@@ -787,8 +787,86 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // 8-bit q / k: the 16 lanes that hold one token row of a slab hold one whole head
   static_assert(EPI != EPI_PACK8 || SW % 128 == 0, "8-bit q / k need head-aligned slabs");
   const bool vt_tile = PACK && n0 >= g.nq + g.nk && g.c_rpb % BM == 0;
+  // Phase 2 item it of a thread is chunk idx = tid + it * NT of the slab (row
+  // idx / CPRS, columns 8 * (idx % CPRS) ..+7).  When NT is a multiple of CPRS the
+  // chunk's columns are the same in every item, so the bias (and the gate of a
+  // residual) is fetched once per slab.
+  constexpr int CPRS = SW / 8, TOT = BM * CPRS, IT = (TOT + NT - 1) / NT;
+  constexpr bool FIXC = NT % CPRS == 0;
+  constexpr bool PRE_R = EPI == EPI_PACK || EPI == EPI_PACK8;
+  // batch items a residual tile's rows span: two gate rows cover the tile when the
+  // items are at least a tile long
+  const int gb_lo = m0 / g.c_rpb, gb_hi = min(m0 + BM - 1, g.M - 1) / g.c_rpb;
+  const bool gate2 = FIXC && gb_hi - gb_lo <= 1;
+  // residual epilogue without global loads in phase 2: the thread's chunk columns
+  // are fixed (bias and gates fetched once per slab) and the residual rows are
+  // fetched in two batches
+  const bool fast_x = EPI == EPI_RESID && FIXC && (gate2 || !g.gate);
 #pragma unroll
   for (int s0 = 0; s0 < BN; s0 += SW) {
+    const int nbase = n0 + s0;
+    int sec = 0;
+    if (PACK) sec = nbase < g.nq ? 0 : (nbase < g.nq + g.nk ? 1 : 2);
+    // Global inputs of this thread's phase-2 items (residual rows, gates, RoPE
+    // rows, bias) are fetched before the slab is staged, so their latency overlaps
+    // the LDS staging and the barrier: an item waiting for its own load puts one
+    // HBM round trip per item on the tile's critical path (one workgroup per CU
+    // leaves nothing else to run meanwhile).
+    // residual rows: registers for half the items (the other half is fetched in
+    // one batch once the first half is done), which keeps the tile's accumulators
+    // of the next slab and these rows within the register budget
+    constexpr int NPX = EPI == EPI_RESID ? (IT + 1) / 2 : 1;
+    f32x4 pre[PRE_R ? IT : NPX][2];
+    auto load_x = [&](int it, int slot) {
+      const int idx = tid + it * NT;
+      const int lrow = idx / CPRS, row = m0 + lrow;
+      if (idx >= TOT || row >= g.M) return;
+      long long xrow = row;
+      if (g.c_valid > 0) {
+        const int b = row / g.c_rpb, t = row - b * g.c_rpb;
+        if (t >= g.c_valid) return;
+        xrow = (long long)b * g.c_valid + t;
+      }
+      const float* xp = g.x + xrow * g.ldx + nbase + (idx % CPRS) * 8;
+      pre[slot][0] = *reinterpret_cast<const f32x4*>(xp);
+      pre[slot][1] = *reinterpret_cast<const f32x4*>(xp + 4);
+    };
+    f32x4 pbias[2], pgate[2][2];
+    const int c8f = (tid % CPRS) * 8;
+    if (FIXC && g.bias && !(PACK && vt_tile)) {
+      pbias[0] = *reinterpret_cast<const f32x4*>(g.bias + nbase + c8f);
+      pbias[1] = *reinterpret_cast<const f32x4*>(g.bias + nbase + c8f + 4);
+    }
+    if (fast_x) {
+      if (g.gate) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* gp = g.gate + (long long)(h ? gb_hi : gb_lo) * g.gate_bstride + nbase + c8f;
+          pgate[h][0] = *reinterpret_cast<const f32x4*>(gp);
+          pgate[h][1] = *reinterpret_cast<const f32x4*>(gp + 4);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < NPX; ++it) load_x(it, it);
+    }
+    if constexpr (PRE_R) {
+      if (g.rope && sec < 2 && !vt_tile) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int idx = tid + it * NT;
+          const int lrow = idx / CPRS, row = m0 + lrow;
+          if (idx >= TOT || row >= g.M) continue;
+          const int n = nbase + (idx % CPRS) * 8;
+          const int nsec = n - (sec == 0 ? 0 : g.nq);
+          const int e0 = nsec % g.hd;
+          const int t = row % g.c_rpb;
+          if (g.c_valid > 0 && t >= g.c_valid) continue;
+          const f32x4* rp = reinterpret_cast<const f32x4*>(g.rope + (long long)t * (g.hd / 2) + e0 / 2);
+          pre[it][0] = rp[0];
+          pre[it][1] = rp[1];
+        }
+      }
+    }
     // phase 1: the accumulators hold C^T (the weight fragment is the MFMA row
     // operand), so element r of lane l is column 8*(r/4) + 4*g2 + r%4, row l32 of
     // its 32x32 block: four consecutive columns per lane, one 16-byte LDS write
@@ -817,9 +895,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
     __syncthreads();
     // phase 2
-    const int nbase = n0 + s0;
-    int sec = 0;
-    if (PACK) sec = nbase < g.nq ? 0 : (nbase < g.nq + g.nk ? 1 : 2);
     if (PACK && vt_tile) {
       // v^T from the transposed slab.  Lane work item (column, 16-token group,
       // half hf): tokens 4hf..4hf+3 and 8+4hf..8+4hf+3 of the group, which the
@@ -892,10 +967,52 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
         }
       }
+    } else if (EPI == EPI_RESID && fast_x) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        if (it == NPX) {
+#pragma unroll
+          for (int i2 = NPX; i2 < IT; ++i2) load_x(i2, i2 - NPX);
+        }
+        const int idx = tid + it * NT;
+        if (idx >= TOT) break;
+        const int lrow = idx / CPRS, row = m0 + lrow;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(&slab[lrow * SWP + c8f]);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(&slab[lrow * SWP + c8f + 4]);
+        f32x4 y0 = lo, y1 = hi;
+        if (g.bias) {
+          y0 += pbias[0];
+          y1 += pbias[1];
+        }
+        f32x4 x0 = pre[it % NPX][0], x1 = pre[it % NPX][1];
+        const int b = row / g.c_rpb, t = row - b * g.c_rpb;
+        if (g.gate) {
+          const bool h = b != gb_lo;
+          const f32x4 g0 = h ? pgate[1][0] : pgate[0][0];
+          const f32x4 g1 = h ? pgate[1][1] : pgate[0][1];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            x0[u] += g0[u] * y0[u];
+            x1[u] += g1[u] * y1[u];
+          }
+        } else {
+          x0 += y0;
+          x1 += y1;
+        }
+        if (row < g.M && (g.c_valid <= 0 || t < g.c_valid)) {
+          const long long xrow = g.c_valid > 0 ? (long long)b * g.c_valid + t : (long long)row;
+          float* xp = g.x + xrow * g.ldx + nbase + c8f;
+          *reinterpret_cast<f32x4*>(xp) = x0;
+          *reinterpret_cast<f32x4*>(xp + 4) = x1;
+        }
+      }
     } else {
-      for (int idx = tid; idx < BM * (SW / 8); idx += NT) {
-        const int lrow = idx / (SW / 8);
-        const int c8 = (idx % (SW / 8)) * 8;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int idx = tid + it * NT;
+        if (idx >= TOT) break;
+        const int lrow = idx / CPRS;
+        const int c8 = (idx % CPRS) * 8;
         const int row = m0 + lrow;
         if (row >= g.M) continue;
         const int n = nbase + c8;
@@ -908,8 +1025,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           v[4 + u] = hi[u];
         }
         if (g.bias) {
-          const f32x4 b0 = *reinterpret_cast<const f32x4*>(g.bias + n);
-          const f32x4 b1 = *reinterpret_cast<const f32x4*>(g.bias + n + 4);
+          f32x4 b0, b1;
+          if constexpr (FIXC) {
+            b0 = pbias[0];
+            b1 = pbias[1];
+          } else {
+            b0 = *reinterpret_cast<const f32x4*>(g.bias + n);
+            b1 = *reinterpret_cast<const f32x4*>(g.bias + n + 4);
+          }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             v[u] += b0[u];
@@ -1006,10 +1129,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           const int hh = nsec / g.hd, e0 = nsec - hh * g.hd;
           const int b = row / g.c_rpb, t = row - b * g.c_rpb;
           if (g.c_valid > 0 && t >= g.c_valid) continue;  // padding row
-          if (g.rope) {
+          if (g.rope && sec < 2) {
             // per-token (cos, sin) of the four pairs (e0, e0+1) .. (e0+6, e0+7)
-            const f32x4* rp = reinterpret_cast<const f32x4*>(g.rope + (long long)t * (g.hd / 2) + e0 / 2);
-            const f32x4 c01 = rp[0], c23 = rp[1];
+            const f32x4 c01 = pre[it][0], c23 = pre[it][1];
             const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
 #pragma unroll
             for (int u = 0; u < 8; u += 2) {
