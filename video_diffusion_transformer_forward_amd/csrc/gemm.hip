@@ -793,7 +793,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // residual) is fetched once per slab.
   constexpr int CPRS = SW / 8, TOT = BM * CPRS, IT = (TOT + NT - 1) / NT;
   constexpr bool FIXC = NT % CPRS == 0;
-  constexpr bool PRE_R = EPI == EPI_PACK || EPI == EPI_PACK8;
   // batch items a residual tile's rows span: two gate rows cover the tile when the
   // items are at least a tile long
   const int gb_lo = m0 / g.c_rpb, gb_hi = min(m0 + BM - 1, g.M - 1) / g.c_rpb;
@@ -807,8 +806,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int nbase = n0 + s0;
     int sec = 0;
     if (PACK) sec = nbase < g.nq ? 0 : (nbase < g.nq + g.nk ? 1 : 2);
-    // Global inputs of this thread's phase-2 items (residual rows, gates, RoPE
-    // rows, bias) are fetched before the slab is staged, so their latency overlaps
+    // Global inputs of this thread's phase-2 items (residual rows, gates, bias)
+    // are fetched before the slab is staged, so their latency overlaps
     // the LDS staging and the barrier: an item waiting for its own load puts one
     // HBM round trip per item on the tile's critical path (one workgroup per CU
     // leaves nothing else to run meanwhile).
@@ -816,7 +815,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     // one batch once the first half is done), which keeps the tile's accumulators
     // of the next slab and these rows within the register budget
     constexpr int NPX = EPI == EPI_RESID ? (IT + 1) / 2 : 1;
-    f32x4 pre[PRE_R ? IT : NPX][2];
+    f32x4 pre[NPX][2];
     auto load_x = [&](int it, int slot) {
       const int idx = tid + it * NT;
       const int lrow = idx / CPRS, row = m0 + lrow;
@@ -848,24 +847,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
 #pragma unroll
       for (int it = 0; it < NPX; ++it) load_x(it, it);
-    }
-    if constexpr (PRE_R) {
-      if (g.rope && sec < 2 && !vt_tile) {
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-          const int idx = tid + it * NT;
-          const int lrow = idx / CPRS, row = m0 + lrow;
-          if (idx >= TOT || row >= g.M) continue;
-          const int n = nbase + (idx % CPRS) * 8;
-          const int nsec = n - (sec == 0 ? 0 : g.nq);
-          const int e0 = nsec % g.hd;
-          const int t = row % g.c_rpb;
-          if (g.c_valid > 0 && t >= g.c_valid) continue;
-          const f32x4* rp = reinterpret_cast<const f32x4*>(g.rope + (long long)t * (g.hd / 2) + e0 / 2);
-          pre[it][0] = rp[0];
-          pre[it][1] = rp[1];
-        }
-      }
     }
     // phase 1: the accumulators hold C^T (the weight fragment is the MFMA row
     // operand), so element r of lane l is column 8*(r/4) + 4*g2 + r%4, row l32 of
@@ -1129,9 +1110,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           const int hh = nsec / g.hd, e0 = nsec - hh * g.hd;
           const int b = row / g.c_rpb, t = row - b * g.c_rpb;
           if (g.c_valid > 0 && t >= g.c_valid) continue;  // padding row
-          if (g.rope && sec < 2) {
+          if (g.rope) {
             // per-token (cos, sin) of the four pairs (e0, e0+1) .. (e0+6, e0+7)
-            const f32x4 c01 = pre[it][0], c23 = pre[it][1];
+            const f32x4* rp = reinterpret_cast<const f32x4*>(g.rope + (long long)t * (g.hd / 2) + e0 / 2);
+            const f32x4 c01 = rp[0], c23 = rp[1];
             const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
 #pragma unroll
             for (int u = 0; u < 8; u += 2) {
