@@ -164,7 +164,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     tm = lid / nn;
     tn = lid - tm * nn;
   } else {
-    constexpr int GM = 8;
+    // groups of GM M-tiles walk all N-tiles, M fastest.  Eight 256-row bf16 A
+    // panels of K <= 2048 (up to 1 MB each) overflow one XCD's 4 MB L2 while four
+    // fit; with many N-tiles (the FFN1 shape: 35) the smaller group reuses its A
+    // panels from L2 (5% faster there; 8 stays better for fewer N-tiles)
+    const int GM = (LOADER == LOAD_PLAIN && sizeof(T) == 2 && nn >= 32 && g.K <= 2048) ? 4 : 8;
     const int group = lid / (GM * nn);
     const int first_m = group * GM;
     const int gsize = min(nm - first_m, GM);
