@@ -16,7 +16,7 @@
 // while the current step's MFMAs run.  Tile rows hold 16-byte chunks whose
 // position is XOR-swizzled with low row bits, which puts the 16 rows one
 // wave-wide operand read touches on distinct banks.  Tiles are ordered in groups
-// of 8 M-tiles and the hardware workgroup order is remapped so that each XCD
+// of 8 (or 4) M-tiles and the hardware workgroup order is remapped so that each XCD
 // (with its own L2) works through one contiguous range.  The epilogue stages
 // the fp32 tile in LDS and writes 16-byte pieces.
 #include "common.h"
@@ -152,7 +152,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int g2 = lane >> 5;  // lane group: which 8-chunk of a 16-wide k step
   const int l32 = lane & 31;
 
-  // ---- tile coordinates: XCD-contiguous ranges, groups of 8 M-tiles
+  // ---- tile coordinates: XCD-contiguous ranges, groups of 8 or 4 M-tiles
   const int nm = (g.M + BM - 1) / BM;
   const int nn = g.N / BN;
   const int ntiles = nm * nn;
