@@ -404,7 +404,7 @@ hipError_t launch_ln_mod(const float* x, void* out, int rows, int D, int rows_pe
   if (rows <= 0) return hipSuccess;
   if (D % 256 != 0 || D / 256 > LN_MAX_V4) return hipErrorInvalidValue;
   if ((shift == nullptr) != (scale == nullptr)) return hipErrorInvalidValue;
-  constexpr int R = 8;  // rows per wave in the narrow-row kernel
+  constexpr int R = 2;  // rows per wave in the narrow-row kernel (2: 4x the workgroups of 8, a shorter last round; 6% faster)
   const dim3 grid_r((rows + 4 * R - 1) / (4 * R));
   T* o = reinterpret_cast<T*>(out);
   switch (D / 256) {
