@@ -384,7 +384,7 @@ hipError_t launch_ln_mod8(const float* x, unsigned char* out8, unsigned char* sc
   q8.sc = sc;
   q8.sc_ld = sc_ld;
   q8.pitch = pitch;
-  constexpr int R = 8;
+  constexpr int R = 2;  // rows per wave, as in launch_ln_mod
   const dim3 grid_r((rows + 4 * R - 1) / (4 * R));
   bf16* o = nullptr;
   switch (D / 256) {
