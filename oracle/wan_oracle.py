@@ -295,7 +295,8 @@ def _lin(x, w, b):
     return f64(x) @ f64(w).T + f64(b)
 
 
-def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8=False, fp8=False):
+def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8=False, fp8=False,
+                   qk8_exact=False):
     """Self-attention sublayer output (before its gate).
 
     q, k, v = m W_qkv^T + b_qkv (rows of W_qkv ordered [q; k; v]); RoPE on q and
@@ -311,6 +312,8 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8
     operand precision of the projection in bf16 mode), see round_bf16_rne.
     fp8: the q, k, v projection is an 8-bit GEMM (linear_fp8); q and k are then
     decided on as that GEMM gives them (implies qk8).
+    qk8_exact: take the 8-bit decision on q and k projected from the exact m
+    instead (the plain reading, with no rounding of the projection input).
     """
     qk8 = qk8 or fp8
     if attn is not None:
@@ -321,7 +324,7 @@ def self_attention(m_all, w, heads, grid, rows=None, attn=None, record=None, qk8
     wq, wk, wv = np.split(f64(w["qkv_w"]), 3, axis=0)
     bq, bk, bv = np.split(f64(w["qkv_b"]), 3)
     lin = linear_fp8 if fp8 else _lin
-    m_qk = round_bf16_rne(m_all) if qk8 and not fp8 else m_all
+    m_qk = round_bf16_rne(m_all) if qk8 and not fp8 and not qk8_exact else m_all
     k = rope_apply(lin(m_qk, wk, bk).reshape(B, L, heads, d), grid).reshape(B, L, D)
     v = lin(m_all, wv, bv)
     mq = m_qk if rows is None else m_qk[:, rows]
@@ -363,7 +366,8 @@ def ffn(xm, w, fp8=False):
     return lin(gelu(lin(xm, w["ff1_w"], w["ff1_b"])), w["ff2_w"], w["ff2_b"])
 
 
-def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, record=None, qk8=False, fp8=False):
+def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, record=None, qk8=False, fp8=False,
+              qk8_exact=False):
     """One DiT block, residual stream in float64.
 
         x <- x + g1 * SA(LN(x) (1 + sc1) + sh1)
@@ -376,7 +380,8 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
     rows: if given, return only those tokens' outputs (the keys and values of
     self-attention still come from every token) -> (B, len(rows), D).
     attn / record: see self_attention (diffusion cache); qk8: 8-bit q k^T in self-attention;
-    fp8: the q/k/v, cross-attention query and both FFN projections as 8-bit GEMMs, plus qk8.
+    fp8: the q/k/v, cross-attention query and both FFN projections as 8-bit GEMMs, plus qk8;
+    qk8_exact: see self_attention.
     """
     x = f64(x)
     mod = f64(mod)
@@ -390,7 +395,7 @@ def dit_block(x, mod, ctx, w, heads, grid, img_len=0, rows=None, attn=None, reco
     if mod.ndim == 4 and rows is not None:
         g1, sh2, sc2, g2 = [a[:, rows] for a in (g1, sh2, sc2, g2)]
     xr = x if rows is None else x[:, rows]
-    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record, qk8, fp8)
+    xr = xr + g1 * self_attention(m_all, w, heads, grid, rows, attn, record, qk8, fp8, qk8_exact)
     xr = xr + cross_attention(layer_norm(xr), ctx, w, heads, img_len, fp8)
     xr = xr + g2 * ffn(modulate(layer_norm(xr), sh2, sc2), w, fp8)
     return xr

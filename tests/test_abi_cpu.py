@@ -230,3 +230,37 @@ def test_vae_shapes_and_argument_errors():
     assert dec(0, 1, cb=16) == N.WAN_E_WORKSPACE
     assert dec(0, 1, z=None) == N.WAN_E_NULL
     assert dec(0, 1, z=F + 4) == N.WAN_E_ALIGN
+
+
+def test_vae_device_rounds_weights_to_nearest_even():
+    """VaeDevice converts float32 weights that are not bf16-exact to the nearest bf16 value,
+    ties to even (the DiT weights' conversion), and keeps biases and scales in float32."""
+    import numpy as np
+    import torch
+    from video_diffusion_transformer_forward_amd import vae_synth as VS
+    import video_diffusion_transformer_forward_amd as W
+    cfg = VS.get_vae_config("vae_tiny")
+    sh = W.vae_shape_of(cfg)
+    params = VS.vae_params(cfg)
+    rng = np.random.default_rng(7)
+    noisy = {}
+    for k, v in params.items():
+        a = np.asarray(v, np.float32)
+        # add sub-bf16 bits so the float32 values are not bf16-exact
+        noisy[k] = (a * (1.0 + rng.uniform(-3e-3, 3e-3, a.shape))).astype(np.float32)
+    name, kind, dims, off, cnt = next(t for t in W.vae_param_table(sh) if t[1] == 0)
+    a = noisy[name].reshape(-1)
+    # plant exact ties: the lower 16 bits 0x8000, once with an even and once with an odd upper half
+    u = a.view(np.uint32)
+    u[0] = np.uint32(0x3F808000)   # 1.00390625: halfway between 0x3F80 and 0x3F81 -> even 0x3F80
+    u[1] = np.uint32(0x3F818000)   # halfway between 0x3F81 and 0x3F82 -> even 0x3F82
+    u[2] = np.uint32(0x3F80C000)   # above the midpoint -> 0x3F81
+    dev = W.VaeDevice(sh, noisy, device="cpu")
+    got = dev.weights.numpy().view(np.uint16)[off:off + cnt]
+    want = (torch.from_numpy(a.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(got, want)
+    assert got[0] == 0x3F80 and got[1] == 0x3F82 and got[2] == 0x3F81
+    # truncation would differ on a sizeable share of these values
+    assert np.mean(got != (a.view(np.uint32) >> 16).astype(np.uint16)) > 0.2
+    fname, _, _, foff, fcnt = next(t for t in W.vae_param_table(sh) if t[1] != 0)
+    np.testing.assert_array_equal(dev.fparams.numpy()[foff:foff + fcnt], noisy[fname].reshape(-1))

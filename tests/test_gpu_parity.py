@@ -422,3 +422,38 @@ def test_step_two_videos():
     got = gpu_step(cfg, mw, bw, z, None, cc, cn, 300.0, 0.05, 5.0)
     ref = O.denoise_step(z, None, cc, cn, mw, bw, cfg.heads, 300.0, 0.05, 5.0)
     assert inc_err(got, ref, z) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- depth of the step
+def _depth_sweep(base, depths, rows_fn=None):
+    mw = S.model_weights(base)
+    bw_all = [S.block_weights(base, b) for b in range(max(depths))]
+    z = S.latent(base)
+    cc, cn = S.context(base, "cond"), S.context(base, "null")
+    errs = {}
+    for n in depths:
+        cfg = base.with_(n_blocks=n)
+        announce(f"step {base.name} depth {n}")
+        got = gpu_step(cfg, mw, bw_all[:n], z, None, cc, cn, cfg.timestep, cfg.dt, cfg.guide_scale)
+        ref = O.denoise_step(z, None, cc, cn, mw, bw_all[:n], cfg.heads, cfg.timestep, cfg.dt, cfg.guide_scale)
+        errs[n] = inc_err(got, ref, z)
+        print(f"{base.name} depth {n:2d}: rel err of dt*v {errs[n]:.3e}", flush=True)
+    return errs
+
+
+def test_step_30_blocks_against_oracle_by_depth():
+    """The CFG step with 30 distinct blocks (the 1.3B model's depth) at the mid shape
+    (L = 180, D = 256, head dim 128) against the oracle, and how the bf16 error grows
+    with depth (1, 2, 4, 8, 16, 30 blocks)."""
+    errs = _depth_sweep(S.get_config("mid_step_bf16"), [1, 2, 4, 8, 16, 30])
+    assert max(errs.values()) <= TOL["bf16"]
+
+
+@pytest.mark.slow
+def test_step_30_blocks_13b_width_short_sequence():
+    """The 1.3B model itself (30 blocks, D = 1536, 12 heads of 128, FFN 8960, 512 text
+    tokens, CFG batch 2, g = 5) over a short latent (grid (2, 8, 12), L = 192) against the
+    oracle over the whole output, at depths 1, 10 and 30."""
+    base = S.get_config("wan13b_step").with_(name="wan13b_step_short", frames=2, height=16, width=24)
+    errs = _depth_sweep(base, [1, 10, 30])
+    assert max(errs.values()) <= TOL["bf16"]

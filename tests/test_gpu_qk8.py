@@ -122,3 +122,53 @@ def test_qk8_block_wan13b_full_size_sampled_rows():
     err = inc_err(got[:, rows], ref, x[:, rows])
     print(f"wan13b qk8 sampled rows: rel err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,peaked", [("mid_bf16", False), ("mid_b2_bf16", False), ("mid_i2v_bf16", False),
+                                         ("mid_bf16", True), ("mid_b2_bf16", True)])
+def test_qk8_against_the_unrounded_8bit_reading(name, peaked):
+    """The library against the 8-bit reading taken on q and k projected from the exact
+    (unrounded) modulated input.  The library's projection operand is bf16, which moves
+    about 6% of the e4m3 codes of q and k by one step against that reading, so the bar is
+    derived from the oracle alone: 1e-2 plus the distance d between the two 8-bit readings
+    (decision on bf16 m / on exact m) on the same case.  On peaked softmax inputs the
+    library must also sit well inside the gap between the unrounded 8-bit reading and the
+    plain (non-8-bit) one, i.e. it follows the 8-bit decision."""
+    base = S.get_config(name)
+    cfg = base.with_(qk8=True)
+    if peaked:
+        cfg = cfg.with_(qk_std=float(np.sqrt(4.0 / base.dim)))
+    announce(f"qk8 unrounded reading {name} peaked={peaked}")
+    w, x, mod, ctx = block_case(cfg)
+    if peaked:
+        w["qkv_b"][2 * cfg.dim:] = 0.0
+        w, mod = _sa_only(cfg, w, mod)
+    got = gpu_block(cfg, w, x, mod, ctx)
+    exact8 = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, cfg.img_len, qk8=True, qk8_exact=True)
+    round8 = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, cfg.img_len, qk8=True)
+    plain = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, cfg.img_len)
+    d = inc_err(round8, exact8, x)
+    bar = TOL["bf16"] + d
+    err = inc_err(got, exact8, x)
+    gap = inc_err(plain, exact8, x)
+    print(f"{name} peaked={peaked}: vs unrounded 8-bit {err:.3e} (bar {bar:.3e}, readings apart {d:.3e}); "
+          f"vs bf16-decided 8-bit {inc_err(got, round8, x):.3e}; unrounded 8-bit vs plain {gap:.3e}")
+    assert err <= bar
+    if peaked:
+        assert gap > 2 * TOL["bf16"]
+        assert err < 0.5 * gap
+
+
+def test_qk8_wan13b_full_size_against_the_unrounded_reading():
+    """1.3B block at L = 32760, sampled rows, against the 8-bit reading decided on exact m."""
+    cfg = S.get_config("wan13b_block").with_(qk8=True)
+    announce("qk8 wan13b full size, unrounded reading")
+    w, x, mod, ctx = block_case(cfg)
+    got = gpu_block(cfg, w, x, mod, ctx)
+    rows = sample_rows(cfg.seq_len, 16, seed=11)
+    exact8 = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, 0, rows=rows, qk8=True, qk8_exact=True)
+    round8 = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, 0, rows=rows, qk8=True)
+    d = inc_err(round8, exact8, x[:, rows])
+    err = inc_err(got[:, rows], exact8, x[:, rows])
+    print(f"wan13b qk8 vs unrounded reading {err:.3e} (readings apart {d:.3e})")
+    assert err <= TOL["bf16"] + d

@@ -20,6 +20,9 @@ from gpu_helpers import announce, rel_err, torch, W
 pytestmark = pytest.mark.gpu
 
 TOL_VAE = 2e-2
+# spatial reach of the decoder, in latent pixels, rounded up: 9 3x3 convolutions at the
+# latent resolution, 5 at x2, 5 at x4 and 6 at x8 (one pixel each)
+VAE_REACH = 14
 
 
 def _gpu_decode(cfg, params, z, chunks=None, chunk_cap=None):
@@ -80,8 +83,9 @@ def test_vae_single_latent_frame():
 
 def test_vae_480p_full_size():
     """The 480p x 81-frame decode (21 x 60 x 104 latent, widths 384/384/384/192/96): video frame 0
-    against the oracle's decode of latent frame 0 alone (by causality the same frame), and the
-    whole decode against a chunked one, bit for bit, over the first latent frames."""
+    against the oracle's decode of latent frame 0 alone (by causality the same frame), the
+    whole decode against a chunked one, bit for bit, over the first latent frames, and video
+    frames 0-4 over a window against the oracle's decode of a latent crop."""
     cfg = VS.get_vae_config("vae_480p")
     announce("vae 480p full size")
     p = VS.vae_params(cfg)
@@ -95,3 +99,13 @@ def test_vae_480p_full_size():
     assert err <= TOL_VAE
     part = _gpu_decode(cfg, p, z[:, :3], [1, 2], chunk_cap=2)
     np.testing.assert_array_equal(part, got[:, :part.shape[1]])
+    # video frames 0-4 (latent frames 0 and 1: frames 1-4 come out of both time doublings)
+    # over a window of 8 x 8 latent pixels: the decoder reaches 13.5 latent pixels in space,
+    # so the oracle's decode of a latent crop with a 14-pixel margin holds the whole decode's
+    # values inside the margin (the CPU pins check this on a small decoder)
+    r0, c0, n, mg = 26, 48, 8, VAE_REACH
+    zc = z[:, :2, r0 - mg:r0 + n + mg, c0 - mg:c0 + n + mg]
+    refc = V.vae_decode(zc, p, cfg.dims, cfg.n_res)[:, :, 8 * mg:8 * (mg + n), 8 * mg:8 * (mg + n)]
+    err = rel_err(got[:, :5, 8 * r0:8 * (r0 + n), 8 * c0:8 * (c0 + n)], refc)
+    print(f"480p frames 0-4, 64 x 64 pixel window: rel err {err:.3e}")
+    assert err <= TOL_VAE

@@ -108,6 +108,20 @@ def test_time_modulation_brute_force():
     assert O.silu(0.0) == 0.0
 
 
+def test_silu_matches_torch_and_hand_values():
+    """SiLU(x) = x * sigmoid(x): against torch's float64 routine over small and large inputs
+    of both signs, and values worked by hand."""
+    x = np.concatenate([np.linspace(-40.0, 40.0, 801), rng.standard_normal(500) * 3, [-300.0, -80.0, 80.0, 300.0]])
+    np.testing.assert_allclose(O.silu(x), tF.silu(T(x)).numpy(), rtol=1e-14, atol=1e-300)
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)        # 0.7310585786...
+    assert O.silu(-1.0) == pytest.approx(-1.0 / (1.0 + math.e), rel=1e-15)               # -0.2689414213...
+    assert O.silu(2.0) == pytest.approx(2.0 / (1.0 + math.exp(-2.0)), rel=1e-15)
+    # large positive inputs pass through, large negative ones vanish; SiLU(x) - SiLU(-x) = x
+    assert O.silu(80.0) == pytest.approx(80.0, rel=1e-15)
+    assert abs(O.silu(-80.0)) < 1e-30
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- norms, GELU
 def test_layer_norm_matches_torch_and_moments():
     x = rng.standard_normal((5, 7, 96)) * 3 + 1.5

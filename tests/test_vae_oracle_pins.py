@@ -144,3 +144,35 @@ def test_param_list_covers_the_decoder():
     dec.decode(VS.vae_latent(cfg))
     assert used == set(p)
     assert cfg.dims == (128, 128, 128, 64, 32)
+
+
+def test_silu_matches_torch_and_hand_values():
+    """The decoder's SiLU(x) = x * sigmoid(x): torch float64 over both signs, hand values."""
+    import math
+    x = np.concatenate([np.linspace(-40.0, 40.0, 801), rng.standard_normal(300) * 4, [-300.0, 300.0]])
+    np.testing.assert_allclose(V.silu(x), torch.nn.functional.silu(torch.from_numpy(x)).numpy(), rtol=1e-14,
+                               atol=1e-300)
+    assert V.silu(np.float64(1.0)) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert V.silu(np.float64(-1.0)) == pytest.approx(-1.0 / (1.0 + math.e), rel=1e-15)
+    assert V.silu(np.float64(0.0)) == 0.0
+    np.testing.assert_allclose(V.silu(x) - V.silu(-x), x, rtol=1e-12, atol=1e-12)
+
+
+def test_decoding_a_latent_crop_gives_the_whole_decode_inside_the_reach():
+    """The decoder's spatial reach is 13.5 latent pixels (nine 3x3 convolutions at the latent
+    resolution, five at x2, five at x4, six at x8): decoding a crop of the latent reproduces the
+    whole decode exactly wherever the output lies 14 or more latent pixels inside the crop, and
+    not where it lies closer to the crop's edge (zero padding reaches it there)."""
+    cfg = VS.get_vae_config("vae_tiny").with_(frames=2, height=34, width=36)
+    p = VS.vae_params(cfg)
+    z = VS.vae_latent(cfg)
+    whole = V.vae_decode(z, p, cfg.dims, cfg.n_res)
+    r0, c0, n, mg = 15, 17, 3, 14
+    zc = z[:, :, r0 - mg:r0 + n + mg, c0 - mg:c0 + n + mg]
+    crop = V.vae_decode(zc, p, cfg.dims, cfg.n_res)
+    inner = crop[:, :, 8 * mg:8 * (mg + n), 8 * mg:8 * (mg + n)]
+    np.testing.assert_allclose(inner, whole[:, :, 8 * r0:8 * (r0 + n), 8 * c0:8 * (c0 + n)], rtol=1e-11, atol=1e-11)
+    # one latent pixel closer to the edge is not exact any more
+    m2 = mg - 1
+    edge = crop[:, :, 8 * m2:8 * m2 + 8, 8 * mg:8 * (mg + n)]
+    assert np.abs(edge - whole[:, :, 8 * (r0 - 1):8 * r0, 8 * c0:8 * (c0 + n)]).max() > 1e-9

@@ -217,7 +217,7 @@ class VaeDevice:
 
     def __init__(self, sh: N.WanVaeShape, params: dict, device="cuda"):
         import numpy as np
-        from .synth import bf16_bits
+        from .synth import bf16_bits, round_bf16
         torch = _torch()
         lib = N.load()
         st = ctypes.c_int(0)
@@ -232,7 +232,8 @@ class VaeDevice:
             if a.size != cnt:
                 raise ValueError(f"{name}: {a.size} values, the library expects {cnt}")
             if kind == 0:
-                wb[off:off + cnt] = bf16_bits(a)
+                # nearest bf16 value, ties to even (the conversion the DiT weights get)
+                wb[off:off + cnt] = bf16_bits(round_bf16(a))
             else:
                 fb[off:off + cnt] = a
         self.weights = torch.from_numpy(wb.view(np.int16)).to(device)
