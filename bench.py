@@ -333,9 +333,9 @@ def main():
     ap.add_argument("--no-vae", action="store_true", help="skip timing the 480p x 81-frame VAE decode")
     ap.add_argument("--vae-only", action="store_true",
                     help="time only the VAE decode and print its JSON object (for profiling runs)")
-    ap.add_argument("--block-configs", default="",
-                    help="comma-separated block configurations to time one block forward of "
-                         "(e.g. wan13b_block,wan14b_720p_block,wan14b_i2v_block); reported under 'blocks'")
+    ap.add_argument("--block-configs", default="wan13b_block,wan14b_720p_block,wan14b_i2v_block",
+                    help="comma-separated block configurations to time one block forward of (a single "
+                         "video, rotating over 3 weight sets); reported under 'blocks'; '' skips them")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB -> 1 GiB elementwise copy three times: the "
                          "known-size kernel that scales the HBM byte counters of a counter-collection run")
