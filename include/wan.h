@@ -46,6 +46,7 @@ extern "C" {
 #define WAN_E_WORKSPACE (-5) /* workspace missing or smaller than wan_workspace_bytes() */
 #define WAN_E_HIP (-6)       /* no usable gfx950 device, or a launch failed */
 #define WAN_E_ENTRY (-7)     /* unknown entry id passed to wan_workspace_bytes */
+#define WAN_E_SCRATCH (-8)   /* the shape needs more than WAN_NOALLOC_SCRATCH_BYTES of scratch */
 
 /* precision modes */
 #define WAN_BF16 0 /* bf16 GEMM/attention operands, float32 accumulation */
@@ -181,6 +182,27 @@ int wan_time_embed(const wan_shape* s, const wan_model_weights* w, float timeste
 int wan_dit_block_forward(const wan_shape* s, const wan_block_weights* w, float* x,
                           const float* mod, long long mod_batch_stride, const void* ctx,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * wan_dit_block_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results as
+ * wan_dit_block_forward, except that the workspace is a fixed device array
+ * of WAN_NOALLOC_SCRATCH_BYTES inside the library (one copy per GPU, held
+ * from the library's load until the process ends).  The call allocates and
+ * frees nothing.
+ *   Returns WAN_E_SCRATCH when wan_workspace_bytes(s, WAN_ENTRY_BLOCK, ...)
+ *   exceeds WAN_NOALLOC_SCRATCH_BYTES (checked before anything is enqueued);
+ *   otherwise as wan_dit_block_forward.
+ * Every call on one GPU uses that GPU's single array, which keeps what the
+ * last call left in it; no result depends on those contents (the block
+ * overwrites every value it uses), so nothing needs clearing between calls.
+ * Calls that may overlap on one GPU (other host threads, or concurrent
+ * streams) race on the array and must be serialised by the caller.
+ */
+#define WAN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int wan_dit_block_forward_noalloc(const wan_shape* s, const wan_block_weights* w, float* x, const float* mod,
+                                  long long mod_batch_stride, const void* ctx, void* stream);
 
 /*
  * Output head: per token LN(x) (no affine) then Linear D -> out_ch*4, and the

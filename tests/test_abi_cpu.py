@@ -31,8 +31,9 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     lib = N.load()
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert lib.wan_status_str(code)
+        assert lib.wan_status_str(code) != lib.wan_status_str(42)
     assert b"unknown" in lib.wan_status_str(42)
 
 
@@ -264,3 +265,44 @@ def test_vae_device_rounds_weights_to_nearest_even():
     assert np.mean(got != (a.view(np.uint32) >> 16).astype(np.uint16)) > 0.2
     fname, _, _, foff, fcnt = next(t for t in W.vae_param_table(sh) if t[1] != 0)
     np.testing.assert_array_equal(dev.fparams.numpy()[foff:foff + fcnt], noisy[fname].reshape(-1))
+
+
+def _noalloc_call(cfg="toy", x=FAKE, mod=FAKE, ctx=FAKE, stride=0, weights=None, **kw):
+    lib = N.load()
+    sh = shape_of(get_config(cfg).with_(**kw))
+    bw = weights or N.WanBlockWeights(*([FAKE] * 16))
+    return lib.wan_dit_block_forward_noalloc(ctypes.byref(sh), ctypes.byref(bw), x, mod, stride, ctx, None)
+
+
+def test_noalloc_block_rejects_shapes_beyond_its_scratch_before_any_hip_call():
+    """The no-allocation block entry point takes shapes whose block workspace fits its fixed
+    64 MiB device array and rejects the others with WAN_E_SCRATCH before touching a device."""
+    assert N.NOALLOC_SCRATCH_BYTES == 64 << 20
+    for name in ("wan13b_block", "wan14b_720p_block", "wan14b_i2v_block"):
+        assert workspace_bytes(get_config(name), N.ENTRY_BLOCK) > N.NOALLOC_SCRATCH_BYTES
+        assert _noalloc_call(name) == N.WAN_E_SCRATCH
+    # the 1.3B width over one 480p latent frame (L = 1560) fits; four frames (L = 6240) do not
+    one = get_config("wan13b_block").with_(frames=1)
+    assert workspace_bytes(one, N.ENTRY_BLOCK) <= N.NOALLOC_SCRATCH_BYTES
+    assert workspace_bytes(one.with_(frames=4), N.ENTRY_BLOCK) > N.NOALLOC_SCRATCH_BYTES
+    assert _noalloc_call("wan13b_block", frames=4) == N.WAN_E_SCRATCH
+    for name in TEST_CONFIGS:
+        assert workspace_bytes(get_config(name), N.ENTRY_BLOCK) <= N.NOALLOC_SCRATCH_BYTES
+    assert _noalloc_call(x=None) == N.WAN_E_NULL
+    assert _noalloc_call(ctx=FAKE + 4) == N.WAN_E_ALIGN
+    assert _noalloc_call(stride=5) == N.WAN_E_SHAPE
+    assert _noalloc_call(heads=3) == N.WAN_E_SHAPE
+    w = N.WanBlockWeights(*([FAKE] * 16))
+    w.o_w = None
+    assert _noalloc_call(weights=w) == N.WAN_E_NULL
+
+
+def test_noalloc_block_without_device_is_a_hip_error():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    assert _noalloc_call() == N.WAN_E_HIP
+    assert _noalloc_call("wan13b_block", frames=1) == N.WAN_E_HIP

@@ -15,7 +15,8 @@ from .synth import WanConfig
 
 __all__ = ["shape_of", "DeviceBlock", "DeviceModel", "workspace", "workspace_bytes", "patchify", "time_embed",
            "cache_bytes", "diffusion_cache", "denoise_step_cached",
-           "dit_block_forward", "head", "denoise_step", "timing_enable", "timing_read", "WanError",
+           "dit_block_forward", "dit_block_forward_noalloc", "head", "denoise_step", "timing_enable", "timing_read",
+           "WanError",
            "vae_shape_of", "vae_param_table", "VaeDevice", "vae_workspace", "vae_cache", "vae_decode",
            "stream_workspace", "stream_tick"]
 
@@ -127,6 +128,18 @@ def dit_block_forward(cfg, block: DeviceBlock, x, mod, ctx, ws, mod_batch_stride
         mod_batch_stride = 6 * cfg.dim if mod.dim() == 3 else 0
     N.check(lib.wan_dit_block_forward(ctypes.byref(sh), ctypes.byref(block.struct), _ptr(x), _ptr(mod),
                                       int(mod_batch_stride), _ptr(ctx), _ptr(ws), ws.numel(), _stream(stream)))
+    return x
+
+
+def dit_block_forward_noalloc(cfg, block: DeviceBlock, x, mod, ctx, mod_batch_stride=None, stream=None):
+    """wan_dit_block_forward_noalloc: one block in place on x, on the library's fixed device scratch
+    (no workspace argument; WanError WAN_E_SCRATCH when the shape needs more than it holds)."""
+    lib = N.load()
+    sh = shape_of(cfg)
+    if mod_batch_stride is None:
+        mod_batch_stride = 6 * cfg.dim if mod.dim() == 3 else 0
+    N.check(lib.wan_dit_block_forward_noalloc(ctypes.byref(sh), ctypes.byref(block.struct), _ptr(x), _ptr(mod),
+                                              int(mod_batch_stride), _ptr(ctx), _stream(stream)))
     return x
 
 

@@ -15,6 +15,8 @@ WAN_E_ALIGN = -4
 WAN_E_WORKSPACE = -5
 WAN_E_HIP = -6
 WAN_E_ENTRY = -7
+WAN_E_SCRATCH = -8
+NOALLOC_SCRATCH_BYTES = 64 << 20   # WAN_NOALLOC_SCRATCH_BYTES
 
 WAN_BF16 = 0
 WAN_FP32 = 1
@@ -28,7 +30,7 @@ ENTRY_TIME_EMBED = 3
 ENTRY_HEAD = 4
 
 EXPORTS = ("wan_status_str", "wan_workspace_bytes", "wan_patchify", "wan_time_embed",
-           "wan_dit_block_forward", "wan_head", "wan_denoise_step", "wan_cache_bytes",
+           "wan_dit_block_forward", "wan_dit_block_forward_noalloc", "wan_head", "wan_denoise_step", "wan_cache_bytes",
            "wan_denoise_step_cached", "wan_timing_enable", "wan_timing_read",
            "wan_stream_workspace_bytes", "wan_stream_tick",
            "wan_vae_param_count", "wan_vae_param_info", "wan_vae_blob_elems", "wan_vae_workspace_bytes",
@@ -106,6 +108,9 @@ def load(path: str = LIB_PATH):
     lib.wan_dit_block_forward.restype = ctypes.c_int
     lib.wan_dit_block_forward.argtypes = [sp, ctypes.POINTER(WanBlockWeights), _vp, _vp, ctypes.c_longlong, _vp,
                                           _vp, ctypes.c_size_t, _vp]
+    lib.wan_dit_block_forward_noalloc.restype = ctypes.c_int
+    lib.wan_dit_block_forward_noalloc.argtypes = [sp, ctypes.POINTER(WanBlockWeights), _vp, _vp, ctypes.c_longlong,
+                                                  _vp, _vp]
     lib.wan_head.restype = ctypes.c_int
     lib.wan_head.argtypes = [sp, ctypes.POINTER(WanModelWeights), _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.wan_denoise_step.restype = ctypes.c_int

@@ -985,6 +985,32 @@ int step_entry(const wan_shape* s, const wan_model_weights* w, float* z, const f
              : run_step<float>(d, w, z, cnd, ctx_cond, ctx_null, timestep, dt, guide_scale, mode, c, ws, p, st);
 }
 
+// Workspace of wan_dit_block_forward_noalloc: a fixed array in device memory,
+// one copy per GPU (allocated by the runtime when the library's code object is
+// loaded on that GPU).  Host code never uses the name itself, which is a
+// host-side stand-in: the device address comes from noalloc_scratch().
+static __device__ __align__(256) unsigned char scratch[WAN_NOALLOC_SCRATCH_BYTES];
+
+namespace wan {
+namespace {
+// Device address of `scratch` on the current device, looked up on the first
+// call on each device (with that device current) and kept; NULL on failure.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+}  // namespace
+}  // namespace wan
+
 extern "C" {
 
 const char* wan_status_str(int code) {
@@ -997,6 +1023,7 @@ const char* wan_status_str(int code) {
     case WAN_E_WORKSPACE: return "workspace missing or too small";
     case WAN_E_HIP: return "no usable gfx950 device, or a HIP launch failed";
     case WAN_E_ENTRY: return "unknown entry id";
+    case WAN_E_SCRATCH: return "the shape needs more scratch than the no-allocation entry point holds";
   }
   return "unknown status code";
 }
@@ -1063,6 +1090,27 @@ int wan_dit_block_forward(const wan_shape* s, const wan_block_weights* w, float*
   if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
   if ((rc = check_device())) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  return d.mode == WAN_BF16 ? run_block<bf16>(d, d.B, w, x, mod, mod_batch_stride, ctx, ws, p, false, st)
+                            : run_block<float>(d, d.B, w, x, mod, mod_batch_stride, ctx, ws, p, false, st);
+}
+
+int wan_dit_block_forward_noalloc(const wan_shape* s, const wan_block_weights* w, float* x, const float* mod,
+                                  long long mod_batch_stride, const void* ctx, void* stream) {
+  Dims d;
+  int rc = check_shape(s, &d);
+  if (rc) return rc;
+  if ((rc = check_block_weights(w, d))) return rc;
+  if ((rc = check_ptrs({x, mod, ctx}))) return rc;
+  if (mod_batch_stride != 0 && mod_batch_stride != 6LL * d.D) return WAN_E_SHAPE;
+  const BlockPlan p = plan_block(d, d.B, 0);
+  if (p.total > WAN_NOALLOC_SCRATCH_BYTES) return WAN_E_SCRATCH;
+  if ((rc = check_device())) return rc;
+  void* ws = noalloc_scratch();
+  if (!ws) return WAN_E_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // no result depends on what the array held before (the block overwrites every
+  // workspace value it uses; padded key rows are masked by assignment), so the
+  // array is not cleared
   return d.mode == WAN_BF16 ? run_block<bf16>(d, d.B, w, x, mod, mod_batch_stride, ctx, ws, p, false, st)
                             : run_block<float>(d, d.B, w, x, mod, mod_batch_stride, ctx, ws, p, false, st);
 }
