@@ -271,8 +271,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       a_vo[i] = (unsigned)((long long)bb * g.a_bstride + (long long)t * g.lda - (a_tile - reinterpret_cast<const unsigned char*>(g.A)) +
                            swz<RB, CPR>(rt, pp) * 16);
     }
+    // W rows of piece i differ from those of piece i % 2 by a multiple of 2 RPD rows and share
+    // its swizzle (row bits 1..3 depend on i only through i % 2): two lane offsets serve all
+    // pieces, the rest of the row offset goes into the scalar offset
+    static_assert(NB % 2 == 0 && RPD == 8, "W lane offsets by piece parity");
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int rt = (wave * NB + i) * RPD + rlow;
       b_vo[i] = (unsigned)((long long)rt * g.ldw + swz<RB, CPR>(rt, pp) * 16);
     }
@@ -286,7 +290,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     };
     auto dma_b = [&](int t, int d) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(b_ring + (t % 2) * B_SB + (wave * NB + d) * 1024), 16,
-                                               b_vo[d], t * BK, 0, 0);
+                                               b_vo[d % 2], t * BK + (d / 2) * 2 * RPD * (int)g.ldw, 0, 0);
     };
     auto refill = [&](int kt, int d) {
       if (d < NB)
@@ -300,7 +304,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
                                                                          0x00020000);
     const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc((void*)(g.w_scale + n0 + brow0), (short)0, -1,
                                                                          0x00020000);
-    int sa8[TM], sb8[TN], nsa[TM], nsb[TN];
+    // the current tile's scales are packed, one byte per fragment (the MFMA's op_sel picks the
+    // byte: W fragment j, A fragment i); the next tile's arrive one byte per register
+    int sa8p = 0, sb8p = 0, nsa[TM], nsb[TN];
+    static_assert(TM == 2 && TN == 4, "one scale byte per fragment in a 32-bit register (op_sel cases below)");
+    auto pack_scales = [&]() {
+      sa8p = 0;
+      sb8p = 0;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa8p |= (nsa[i] & 0xFF) << (8 * i);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb8p |= (nsb[j] & 0xFF) << (8 * j);
+    };
     auto load_scales = [&](int t, int (&xa)[TM], int (&xb)[TN]) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) xa[i] = __builtin_amdgcn_raw_buffer_load_b8(rca, l32 + 32 * i, t * g.a_sld, 0);
@@ -332,9 +347,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     for (int s0 = 0; s0 < NST - 1; ++s0)
 #pragma unroll
       for (int d = 0; d < NA; ++d) dma_a(min(s0, nk - 1), d);
-    load_scales(0, sa8, sb8);
+    load_scales(0, nsa, nsb);
     wait_vmcnt<0>();
     barrier_lds();
+    pack_scales();
 #pragma unroll
     for (int i = 0; i < TM; ++i) read_a(0, 0, i);
 #pragma unroll
@@ -349,8 +365,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         for (int q = 0; q < NM; ++q) {
           if (ks == 0 && q == 0) load_scales(min(kt + 1, nk - 1), nsa, nsb);
           const int i = q % TM, j = q / TM;
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[j], fa8[i], acc[i][j], 0, 0, 0, sb8[j], 0,
-                                                                      sa8[i]);
+          // op_sel must be an immediate: one case per (W fragment, A fragment), resolved at compile time
+          switch (j * 4 + i) {
+#define WAN_MMA8(J, I)                                                                                          \
+  case J * 4 + I:                                                                                                \
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[j], fa8[i], acc[i][j], 0, 0, J, sb8p, I, sa8p); \
+    break;
+            WAN_MMA8(0, 0) WAN_MMA8(0, 1) WAN_MMA8(1, 0) WAN_MMA8(1, 1)
+            WAN_MMA8(2, 0) WAN_MMA8(2, 1) WAN_MMA8(3, 0) WAN_MMA8(3, 1)
+#undef WAN_MMA8
+          }
           if (last && q == SYNC_SLOT) {
             wait_vmcnt<NA>();  // scales, W and A of tile kt+1 have landed
             barrier_lds();
@@ -368,10 +392,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) sa8[i] = nsa[i];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sb8[j] = nsb[j];
+      pack_scales();
     }
     wait_vmcnt<0>();
     __syncthreads();
