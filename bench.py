@@ -28,15 +28,16 @@ MI355X_FP32_TFLOPS = 157.3
 CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 
 # L2 <-> memory bytes of one self-attention launch, from two counter-collection runs of
-# `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-cache-modes --no-vae --calib-copy` (FETCH_SIZE, then WRITE_SIZE,
-# KiB per dispatch), each scaled by known/counted bytes of the 1 GiB calibration copy in the
-# same run.  Valid only for the kernel sources they were taken on (checked by hash).
+# `bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-cache-modes --no-vae --no-qk8 --block-configs "" --calib-copy`
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean over the 60 self-attention launches), each scaled by
+# known/counted bytes of the 1 GiB calibration copy in the same run.  Valid only for the kernel sources
+# they were taken on (checked by hash).
 ATTN_COUNTERS = {
-    "fetch_kib": 884803.94, "fetch_scale": 1048576 / 524306.33,
+    "fetch_kib": 884806.57, "fetch_scale": 1048576 / 524302.75,
     "write_kib": 196560.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "408ac36191ea87a51627792c2abb3f63087cc2c990e425edd0a2df6e3ddac6da",
+    "sha256": "301b53250ef7d834b52a16d5b1dff4b6ef8841efd91055b839d99a0d6db1fcb4",
 }
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 

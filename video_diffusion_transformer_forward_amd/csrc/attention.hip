@@ -42,6 +42,27 @@ __device__ __forceinline__ int att_swz(int r, int c) {
     return c ^ (r & 7);                    // float, 8 chunks of 32 bytes
 }
 
+// Write a lane's share of O^T (query `row`; d = 32 db + 8 r4 + 4 g2 + 0..3) into
+// the LDS rows [query][d] as 4-element stores, each at the swizzled 8-element
+// chunk of its row, so that the 32 rows one store instruction touches spread over
+// the banks (unswizzled, rows of 128 bf16 all start on bank 0: a 32-way conflict).
+template <typename T, int HD>
+__device__ __forceinline__ void stage_o_rows(T* stg, int row, int g2, const f32x16* o, float inv) {
+  constexpr int HC = HD / 8;
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      T* dst = stg + row * HD + att_swz<T, HC>(row, 4 * db + r4) * 8 + 4 * g2;
+      const float v0 = o[db][4 * r4] * inv, v1 = o[db][4 * r4 + 1] * inv;
+      const float v2 = o[db][4 * r4 + 2] * inv, v3 = o[db][4 * r4 + 3] * inv;
+      if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+      else
+        *reinterpret_cast<f32x4*>(dst) = (f32x4){v0, v1, v2, v3};
+    }
+}
+
 template <typename T, int HD>
 struct AttCfg {
   static constexpr int HC = HD / 8;                       // chunks per K row
@@ -263,13 +284,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 
   // ---- epilogue: stage the wave's rows in LDS as [query][d], then 16-byte row stores
   T* st = reinterpret_cast<T*>(smem_raw) + wave * (32 * HD);
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d = 32 * db + 8 * (r / 4) + 4 * g2 + (r % 4);
-      st[l32 * HD + d] = from_f<T>(o[db][r]);
-    }
+  stage_o_rows<T, HD>(st, l32, g2, o, 1.0f);
   __syncthreads();
   const int ld = a.heads * HD;
 #pragma unroll
@@ -279,7 +294,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const int q = q0 + qr;
     if (q < a.Lq) {
       Chunk<T> v;
-      v.load(st + qr * HD + cc * 8);
+      v.load(st + qr * HD + att_swz<T, HC>(qr, cc) * 8);
       v.store(reinterpret_cast<T*>(a.o) + ((long long)b * a.Lq + q) * ld + h * HD + cc * 8);
     }
   }
@@ -706,13 +721,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float inv = 1.0f / (l[qb] + __shfl_xor(l[qb], 32, 64));
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r / 4) + 4 * g2 + (r % 4);
-        stg[(32 * qb + l32) * HD + d] = from_f<T>(o[qb][db][r] * inv);
-      }
+    stage_o_rows<T, HD>(stg, 32 * qb + l32, g2, o[qb], inv);
   }
   __syncthreads();
   const int ld = a.heads * HD;
@@ -723,7 +732,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
     const int q = q0 + qr;
     if (q < a.Lq) {
       Chunk<T> v;
-      v.load(stg + qr * HD + cc * 8);
+      v.load(stg + qr * HD + att_swz<T, HC>(qr, cc) * 8);
       v.store(reinterpret_cast<T*>(a.o) + ((long long)b * a.Lq + q) * ld + h * HD + cc * 8);
     }
   }
@@ -1043,13 +1052,7 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
   T* stg = reinterpret_cast<T*>(smem_raw) + wave * (32 * HD);
   {
     const float inv = 1.0f / (l + __shfl_xor(l, 32, 64));
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r / 4) + 4 * g2 + (r % 4);
-        stg[l32 * HD + d] = from_f<T>(o[db][r] * inv);
-      }
+    stage_o_rows<T, HD>(stg, l32, g2, o, inv);
   }
   __syncthreads();
   const int ld = a.heads * HD;
@@ -1060,7 +1063,7 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
     const int q = q0 + qr;
     if (q < a.Lq) {
       Chunk<T> v;
-      v.load(stg + qr * HD + cc * 8);
+      v.load(stg + qr * HD + att_swz<T, HC>(qr, cc) * 8);
       v.store(reinterpret_cast<T*>(a.o) + ((long long)b * a.Lq + q) * ld + h * HD + cc * 8);
     }
   }

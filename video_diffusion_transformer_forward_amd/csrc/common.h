@@ -72,6 +72,13 @@ template <typename T> __device__ __forceinline__ float to_f(T x);
 template <> __device__ __forceinline__ float to_f<bf16>(bf16 x) { return bf16_to_f(x); }
 template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
 
+// Two floats as bf16 (round to nearest even) in one 32-bit word, the first in the low half.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {to_bf16(lo), to_bf16(hi)};
+  return __builtin_bit_cast(unsigned, v);
+}
+
 // Pack 8 floats into a chunk of T.
 __device__ __forceinline__ void pack8(Chunk<bf16>& c, const float* f) {
   bf16x8 v;
