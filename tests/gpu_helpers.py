@@ -121,3 +121,16 @@ def sample_rows(L, n, seed=0):
     rows = set(rng.choice(L, size=min(n, L), replace=False).tolist())
     rows.update([0, L - 1])
     return sorted(rows)
+
+
+def self_attention_only(cfg, w, mod):
+    """Block weights and modulation under which the block adds only its self-attention sublayer,
+    with b_v = 0 (the output is pure weighting): cross-attention output projection and FFN gate zero."""
+    w = dict(w)
+    w["qkv_b"] = w["qkv_b"].copy()
+    w["qkv_b"][2 * cfg.dim:] = 0.0
+    w["co_w"] = np.zeros_like(w["co_w"])
+    w["co_b"] = np.zeros_like(w["co_b"])
+    m = mod.copy()
+    m[:, 5] = 0.0
+    return w, m

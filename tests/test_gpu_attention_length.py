@@ -23,7 +23,7 @@ import pytest
 from oracle import wan_oracle as O
 from video_diffusion_transformer_forward_amd import synth as S
 
-from gpu_helpers import TOL, announce, block_case, gpu_block, inc_err, sample_rows
+from gpu_helpers import TOL, announce, block_case, gpu_block, inc_err, sample_rows, self_attention_only
 
 pytestmark = pytest.mark.gpu
 
@@ -42,17 +42,6 @@ def _plants(L):
     return {0: (L - 3, 7), 1: (last_full + 29, 301), 2: (L // 2 + 17, 555), 3: (5, 1201)}
 
 
-def _self_attention_only(cfg, w, mod):
-    w = dict(w)
-    w["qkv_b"] = w["qkv_b"].copy()
-    w["qkv_b"][2 * cfg.dim:] = 0.0                   # b_v = 0
-    w["co_w"] = np.zeros_like(w["co_w"])
-    w["co_b"] = np.zeros_like(w["co_b"])
-    m = mod.copy()
-    m[:, 5] = 0.0                                     # FFN gate
-    return w, m
-
-
 def _case(L, kind, qk8):
     base = LENGTHS[L]
     cfg = base.with_(qk8=qk8)
@@ -60,7 +49,7 @@ def _case(L, kind, qk8):
         cfg = cfg.with_(qk_std=float(np.sqrt(4.0 / base.dim)))
     assert cfg.seq_len == L
     w, x, mod, ctx = block_case(cfg)
-    w, mod = _self_attention_only(cfg, w, mod)
+    w, mod = self_attention_only(cfg, w, mod)
     extra = []
     if kind == "planted":
         D, d = cfg.dim, cfg.head_dim

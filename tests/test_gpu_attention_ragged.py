@@ -1,0 +1,48 @@
+"""Self-attention parity over ragged sequence lengths at the 1.3B width (D = 1536, 12 heads of 128, one video).
+
+The bf16 path picks its kernel by the number of 256-query workgroups: from 512 of them
+(L > 10752 at 12 heads and one video) the 8-wave form, below it the 4-wave form of 128
+queries.  These lengths sit on both sides of that switch and give every remainder class of
+the 64-key tile (the keys past L masked in the last tile) and of the 256-query tile (the
+queries past L neither loaded nor stored):
+  10000 = (1, 100, 100): 4-wave form, 16 keys in the last tile;
+  10961 = (1, 97, 113): 17 keys; 11000 = (1, 100, 110): 56 keys, 248 queries in the last tile;
+  11008 = (2, 43, 128): whole tiles; 11021 = (1, 107, 103): 13 keys, 13 queries in the last tile.
+Logits of std about 4 (q / k weights of std sqrt(4/D)), b_v = 0 and only the self-attention
+sublayer, so the output is all weighting and the online-softmax rescale fires late; bf16 and
+8-bit-score modes, sampled query rows (always the first and the last) against the oracle at
+the bf16 bar.
+"""
+import numpy as np
+import pytest
+
+from oracle import wan_oracle as O
+from video_diffusion_transformer_forward_amd import synth as S
+
+from gpu_helpers import TOL, announce, block_case, gpu_block, inc_err, sample_rows, self_attention_only
+
+pytestmark = pytest.mark.gpu
+
+GRIDS = {10000: (1, 100, 100), 10961: (1, 97, 113), 11000: (1, 100, 110), 11008: (2, 43, 128),
+         11021: (1, 107, 103)}
+
+
+@pytest.mark.parametrize("qk8", [False, True], ids=["bf16", "qk8"])
+@pytest.mark.parametrize("L", sorted(GRIDS))
+def test_self_attention_ragged_lengths(L, qk8):
+    f, h, w_ = GRIDS[L]
+    base = S.get_config("wan13b_block")
+    cfg = base.with_(name=f"wan13b_L{L}", seed_base=40 + L % 17, frames=f, height=2 * h, width=2 * w_, qk8=qk8,
+                     qk_std=float(np.sqrt(4.0 / base.dim)))
+    assert cfg.seq_len == L and cfg.batch == 1
+    announce(f"self-attention ragged L={L} grid={cfg.grid} qk8={qk8}")
+    w, x, mod, ctx = block_case(cfg)
+    w, mod = self_attention_only(cfg, w, mod)
+    last_q = (L - 1) // 256 * 256
+    rows = sorted(set(sample_rows(L, 12, seed=L) + [last_q, min(last_q + 1, L - 1), L - 2]))
+    got = gpu_block(cfg, w, x, mod, ctx)
+    assert np.all(np.isfinite(got))
+    ref = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, 0, rows=rows, qk8=qk8)
+    err = inc_err(got[:, rows], ref, x[:, rows])
+    print(f"L={L} qk8={qk8}: rel err {err:.3e} over {len(rows)} rows")
+    assert err <= TOL["bf16"]
