@@ -935,6 +935,50 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
   }
 
+  if constexpr (C::MI16 && (EPI == EPI_STORE || EPI == EPI_STORE_GELU)) {
+    // bf16 store epilogues of the 16x16 form: bias (and GELU) on the accumulators, then
+    // the whole tile staged once in LDS as bf16 (half the bytes of the float32 slabs, one
+    // barrier) and written as 16-byte row pieces; each sum sees the same float32
+    // operations as in the general path, so the outputs are the same bits.
+    // A staged row is 32 bytes past a multiple of 256: the 16 rows of one 8-byte write
+    // instruction (32 bytes each) share the 8 bank groups of 32 bytes two by two.
+    constexpr int SP = BN + 16;
+    static_assert((size_t)BM * SP * sizeof(T) <= C::LDS_BYTES, "bf16 staging");
+    T* stage16 = reinterpret_cast<T*>(smem_raw);
+#pragma unroll
+    for (int j = 0; j < TC16; ++j) {
+      const int col = brow0 + 16 * j + 4 * (lane >> 4);
+      f32x4 bj = {0.f, 0.f, 0.f, 0.f};
+      if (g.bias) bj = *reinterpret_cast<const f32x4*>(g.bias + n0 + col);
+#pragma unroll
+      for (int i = 0; i < TR16; ++i) {
+        const int row = arow0 + 16 * i + (lane & 15);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc16[i][j][e] + bj[e];
+          if constexpr (EPI == EPI_STORE_GELU) v[e] = gelu_erf(v[e]);
+        }
+        *reinterpret_cast<uint2*>(stage16 + row * SP + col) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+    __syncthreads();
+    constexpr int CPR16 = BN / 8, IT16 = BM * CPR16 / NT;
+    static_assert(IT16 * NT == BM * CPR16, "whole 16-byte pieces per thread");
+#pragma unroll
+    for (int it = 0; it < IT16; ++it) {
+      const int idx = tid + it * NT;
+      const int lrow = idx / CPR16, c8 = (idx % CPR16) * 8;
+      const int row = m0 + lrow;
+      if (row < g.M) {
+        Chunk<T> c;
+        c.load(stage16 + lrow * SP + c8);
+        c.store(reinterpret_cast<T*>(g.C) + (long long)row * g.ldc + n0 + c8);
+      }
+    }
+    return;
+  }
   // ---- epilogue.  The fp32 tile goes through LDS in column slabs; phase 2
   // walks a slab in 8-element chunks and writes 16-byte pieces.
   float* slab = reinterpret_cast<float*>(smem_raw);
