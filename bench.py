@@ -27,17 +27,18 @@ MI355X_BF16_TFLOPS = 2516.6   # dense bf16 MFMA peak (256 CU x 4096 flop/clk x 2
 MI355X_FP32_TFLOPS = 157.3
 CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 
-# L2 <-> memory bytes of one self-attention launch, from two counter-collection runs of
+# L2 <-> memory bytes of one self-attention launch (the static-offset kernel plus its flagged-workgroup
+# pass), from two counter-collection runs of
 # `bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-cache-modes --no-vae --no-qk8 --block-configs "" --calib-copy`
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean over the 60 self-attention launches), each scaled by
-# known/counted bytes of the 1 GiB calibration copy in the same run.  Valid only for the kernel sources
-# they were taken on (checked by hash).
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, means over the 60 launches of each kernel, summed), each
+# scaled by known/counted bytes of the 1 GiB calibration copy in the same run.  Valid only for the kernel
+# sources they were taken on (checked by hash).
 ATTN_COUNTERS = {
-    "fetch_kib": 884806.57, "fetch_scale": 1048576 / 524302.75,
-    "write_kib": 196560.0, "write_scale": 1048576 / 1048576.0,
+    "fetch_kib": 885011.57 + 117.00, "fetch_scale": 1048576 / 524302.88,
+    "write_kib": 196675.20 + 0.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "301b53250ef7d834b52a16d5b1dff4b6ef8841efd91055b839d99a0d6db1fcb4",
+    "sha256": "1505b499b2859cc7c60b4814903210473bb18578aaebe92e1564c594869120c5",
 }
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 
@@ -496,7 +497,7 @@ def main():
         "block_tflops": round(block_tflops, 2),
         "step_tflop": round(flops / 1e12, 3),
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 3) for k, v in kt.items()},
-        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_wide_kernel<128,2,1,8>)",
+        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_wide_kernel<128,2,1,8,true>, static offset, and its flagged-workgroup pass)",
                      "achieved": round(attn_achieved, 2), "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / MI355X_BF16_TFLOPS, 4), "traffic": attn_traffic_bytes(),
                      "traffic_unit": "bytes per launch (L2-memory fetch + write counters)",

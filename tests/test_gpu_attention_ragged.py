@@ -46,3 +46,33 @@ def test_self_attention_ragged_lengths(L, qk8):
     err = inc_err(got[:, rows], ref, x[:, rows])
     print(f"L={L} qk8={qk8}: rel err {err:.3e} over {len(rows)} rows")
     assert err <= TOL["bf16"]
+
+
+def test_self_attention_static_offset_fallback():
+    """The 256-query bf16 kernel offsets every exponent by |q| max_k |k|, which bounds the scores
+    from above; when that bound overshoots a row's largest score by more than 64 in base 2 the
+    workgroup is recomputed with the running maximum.  Here one token's key in head 0 carries a
+    component of about 800 along feature d-1 (the slowest-turning RoPE pair): the bound of
+    every head-0 query is then hundreds of powers of two above its scores, so all of head 0 takes
+    the recomputation, while the other heads stay on the static offset.  Half of the head-0
+    queries (q_{d-1} > 0) are dominated by that key, the others ignore it."""
+    f, h, w_ = GRIDS[11000]
+    base = S.get_config("wan13b_block")
+    cfg = base.with_(name="wan13b_L11000_fb", seed_base=77, frames=f, height=2 * h, width=2 * w_)
+    L = cfg.seq_len
+    announce(f"self-attention static-offset fallback L={L}")
+    w, x, mod, ctx = block_case(cfg)
+    w, mod = self_attention_only(cfg, w, mod)
+    D, d = cfg.dim, cfg.head_dim
+    tok, j = 4321, 777
+    qkv_w = w["qkv_w"].copy()
+    qkv_w[D + 0 * d + d - 1, j] += 20.0
+    w["qkv_w"] = S.round_bf16(qkv_w)
+    x[:, tok, j] = 1000.0
+    rows = sorted(set(sample_rows(L, 16, seed=5) + [tok, tok + 1]))
+    got = gpu_block(cfg, w, x, mod, ctx)
+    assert np.all(np.isfinite(got))
+    ref = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, 0, rows=rows)
+    err = inc_err(got[:, rows], ref, x[:, rows])
+    print(f"L={L} planted large-norm key: rel err {err:.3e} over {len(rows)} rows")
+    assert err <= TOL["bf16"]

@@ -80,6 +80,9 @@ int check_shape(const wan_shape* s, Dims* d) {
 // Offsets (bytes) inside the workspace of one block run over Bb batch rows.
 struct BlockPlan {
   size_t m, r1, q, k, vt, o, ck, cvt, ik, ivt, rope, ropet;
+  // static-maximum self-attention: partial maxima of |k|^2 per (batch item, head, 256-row
+  // tile, wave of the QKV GEMM) and the per-workgroup fallback flags
+  size_t kmax, aflag;
   // WAN_FP8: e4m3 LayerNorm outputs and their scales, e4m3 FFN hidden and its
   // scales, the block's e4m3 projection weights and their scales
   size_t m8, msc, h8, hsc, w8, wsc;
@@ -143,6 +146,10 @@ BlockPlan plan_block(const Dims& d, int Bb, size_t base) {
   off += al(rope_entries(d) * sizeof(float2));
   p.ropet = off;
   off += al((size_t)d.L * (d.hd / 2) * sizeof(float2));
+  p.kmax = off;
+  off += al((size_t)Bb * d.heads * (pad256(d.L) / 256) * 8 * sizeof(float));
+  p.aflag = off;
+  off += al((size_t)attn_wide_flags(d.L, d.heads, Bb) * sizeof(int));
   p.m8 = p.msc = p.h8 = p.hsc = p.w8 = p.wsc = off;
   if (d.fp8) {
     const size_t rows_p = (size_t)Bb * pad256(d.L);  // padded token rows of the 8-bit GEMMs
@@ -368,6 +375,12 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
   // self-attention sublayer (its attention output optionally written to, or
   // taken from, the diffusion cache)
   T* a_out = attn_mode == ATTN_COMPUTE ? o : reinterpret_cast<T*>(attn_io);
+  // bf16 self-attention at full length: the static-maximum path (the QKV epilogue gathers
+  // max |k|^2 per batch row and head; flagged workgroups are recomputed)
+  const bool static_max = attn_static_max_path(d.hd, d.L, d.heads, Bb, sizeof(T) == 2, d.qk8);
+  float* kpart = reinterpret_cast<float*>(at(ws, p.kmax));
+  const int kpart_n = P / 256 * 8;  // 256-row tiles per batch item x the QKV GEMM's 8 waves
+  int* aflag = reinterpret_cast<int*>(at(ws, p.aflag));
   if (attn_mode != ATTN_REUSE) {
   HIP_TRY(ln(mod + 0 * d.D, mod + 1 * d.D));
   HIP_TRY(launch_zero_vt_pad<T>(at(ws, p.vt), Bb * d.heads, d.hd, d.L, d.Lp, st));
@@ -380,6 +393,10 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     g.q = at(ws, p.q); g.k = at(ws, p.k); g.vt = at(ws, p.vt);
     g.nq = d.D; g.nk = d.D; g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
     g.rope = ropet;
+    if (static_max) {
+      g.kpart = kpart;
+      g.kpart_n = kpart_n;
+    }
     if (d.qk8) {
       // e4m3 q / k take the first half of their bf16 regions, the scale bytes follow
       g.qs = reinterpret_cast<unsigned char*>(at(ws, p.q + qk8_bytes(d, Bb)));
@@ -393,6 +410,11 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     a.q = at(ws, p.q); a.Lq = d.L; a.Lqp = d.Lp;
     a.k[0] = at(ws, p.k); a.vt[0] = at(ws, p.vt); a.Lk[0] = d.L; a.Lkp[0] = d.Lp; a.nsrc = 1; a.self = 1;
     a.o = a_out; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
+    if (static_max) {
+      a.kpart = kpart;
+      a.kpart_n = kpart_n;
+      a.fallback = aflag;
+    }
     if (d.qk8) {
       a.qk8 = 1;
       a.qs = reinterpret_cast<const unsigned char*>(at(ws, p.q + qk8_bytes(d, Bb)));

@@ -347,7 +347,16 @@ __device__ __forceinline__ void att_barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
-template <int HD, int NR, int QB, int NW>
+// SM (static maximum): every query's exponent offset is fixed before the key sweep at
+// m_q = |q| max_k |k| (by Cauchy-Schwarz no score exceeds it, so every probability is at
+// most 1), which removes the per-tile row maxima, the running-max update and the
+// rescaling of the accumulators.  The result is the same softmax; only its scale
+// differs, and exactness needs the largest probability of a row to stay far above
+// the smallest normal float: a workgroup with a row sum below 2^-64 (the offset
+// overshot the true maximum by more than 64 in base 2) flags itself in a.fallback (one
+// flag per wave, written whether set or not), and a second launch of the running-max
+// kernel recomputes exactly those.
+template <int HD, int NR, int QB, int NW, bool SM = false>
 __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   using T = bf16;
   using Cfg = WideCfg<HD, NR, QB, NW>;
@@ -376,6 +385,13 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   const int bh = id / nqt;
   const int b = bh / a.heads;
   const int h = bh - b * a.heads;
+  // second pass after the static-maximum kernel: only the workgroups it flagged (one flag per wave)
+  if (!SM && a.only) {
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= a.only[id * NW + w];
+    if (any == 0) return;
+  }
   const int q0 = qt * BMQ + wave * WQ;
   const float c = a.scale_log2;
   const int Lk = a.Lk[0];
@@ -495,11 +511,34 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
     m[qb] = -INFINITY;
     l[qb] = 0.f;
   }
+  if constexpr (SM) {
+    // m_q = |q| max_k |k|: |q| from the bf16 values the MFMAs multiply, max |k| from the keys
+    // before their rounding to bf16 (which moves a norm by at most 2^-9 of itself); the
+    // factor 1 + 2^-8 covers that and the float32 rounding of the norms and score sums
+    float k2 = 0.f;
+    for (int i = lane; i < a.kpart_n; i += 64) k2 = __builtin_elementwise_maximum(k2, a.kpart[(long long)bh * a.kpart_n + i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) k2 = __builtin_elementwise_maximum(k2, __shfl_xor(k2, o, 64));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float q2 = 0.f;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const bf16x8 e = as_bf16x8(qf[qb][st].v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q2 = __builtin_fmaf((float)e[u], (float)e[u], q2);
+      }
+      q2 += __shfl_xor(q2, 32, 64);
+      m[qb] = sqrtf(q2 * k2) * (1.0f + 1.0f / 256.0f);
+    }
+  }
 
   // Lazy running max: a query's max moves only when its tile max exceeds it by
   // more than 2^8; its sum is then scaled by alpha at once, the accumulators
   // (only when some lane of the wave moved) once the pending P V products are in.
   float alpha[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) alpha[qb] = 1.0f;
   auto new_max = [&](const float (&mx)[QB]) {
     bool moved = false;
 #pragma unroll
@@ -580,8 +619,10 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   scores(S, 0, 0);
   scores(S, 0, 1);
   mask(S, 0);
-  rowmax(S, mx);
-  new_max(mx);  // first tile: the max moves from -inf, sums and accumulators are still zero
+  if constexpr (!SM) {
+    rowmax(S, mx);
+    new_max(mx);  // first tile: the max moves from -inf, sums and accumulators are still zero
+  }
   probs(S, 0, pf);
   att_barrier_lds();  // K stage 0 is refilled by the first iteration
 
@@ -666,21 +707,23 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
               if (key >= Lk) S[qb][kb][r] = -INFINITY;
             }
         }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          vmax[qb] = __builtin_elementwise_maximum(
-              vmax[qb], __builtin_elementwise_maximum(S[qb][kb][2 * k], S[qb][kb][2 * k + 1]));
-          asm volatile("" : "+v"(vmax[qb]));
-        }
-        if (i == 23) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) mx[qb] = __builtin_elementwise_maximum(vmax[qb], __shfl_xor(vmax[qb], 32, 64));
-          moved = new_max(mx);
-          pin_stats();
+        if constexpr (!SM) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            nmc[qb] = -m[qb] * c;
-            asm volatile("" : "+v"(nmc[qb]));
+            vmax[qb] = __builtin_elementwise_maximum(
+                vmax[qb], __builtin_elementwise_maximum(S[qb][kb][2 * k], S[qb][kb][2 * k + 1]));
+            asm volatile("" : "+v"(vmax[qb]));
+          }
+          if (i == 23) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) mx[qb] = __builtin_elementwise_maximum(vmax[qb], __shfl_xor(vmax[qb], 32, 64));
+            moved = new_max(mx);
+            pin_stats();
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              nmc[qb] = -m[qb] * c;
+              asm volatile("" : "+v"(nmc[qb]));
+            }
           }
         }
       } else {
@@ -715,6 +758,15 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   }
   att_wait_vmcnt<0>();
   __syncthreads();
+  if constexpr (SM) {
+    // a row sum below 2^-64: the static offset overshot this row's largest score by more
+    // than 64 in base 2, so its terms may have fallen below the normal floats
+    bool low = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) low = low || (l[qb] + __shfl_xor(l[qb], 32, 64)) < 0x1p-64f;
+    const int flag = __ballot(low) != 0 ? 1 : 0;
+    if (lane == 0) a.fallback[id * NW + wave] = flag;  // written every time: no clearing needed
+  }
 
   // ---- epilogue: normalise, stage the wave's 64 rows in LDS as [query][d], 16-byte row stores
   T* stg = reinterpret_cast<T*>(smem_raw) + wave * (WQ * HD);
@@ -1082,9 +1134,9 @@ __global__ __launch_bounds__(256, 2) void attn_cross_kernel(const AttnArgs a) {
   attn_body<T, HD, 1, 1>(a);
 }
 // bf16 self-attention: 8 waves of 32 queries (or 4 waves of 32*QB) per workgroup
-template <int HD, int NR, int QB, int NW>
+template <int HD, int NR, int QB, int NW, bool SM>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && QB == 1) ? 2 : 1) void attn_self_wide_kernel(const AttnArgs a) {
-  attn_wide_body<HD, NR, QB, NW>(a);
+  attn_wide_body<HD, NR, QB, NW, SM>(a);
 }
 // bf16 self-attention with 8-bit scores: 8 waves of 32 queries, one workgroup per CU
 template <int NR, int NW>
@@ -1117,10 +1169,10 @@ hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-template <int HD, int NR, int QB, int NW>
+template <int HD, int NR, int QB, int NW, bool SM = false>
 hipError_t launch_attn_wide(const AttnArgs& a, hipStream_t st) {
   using Cfg = WideCfg<HD, NR, QB, NW>;
-  auto kern = attn_self_wide_kernel<HD, NR, QB, NW>;
+  auto kern = attn_self_wide_kernel<HD, NR, QB, NW, SM>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1151,6 +1203,12 @@ hipError_t launch_attn_qk8(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool attn_static_max_path(int hd, int Lq, int heads, int B, bool bf16, bool qk8) {
+  const long long g8 = (long long)((Lq + 255) / 256) * heads * B;
+  return bf16 && !qk8 && hd == 128 && g8 >= 512;
+}
+int attn_wide_flags(int Lq, int heads, int B) { return ((Lq + 255) / 256) * heads * B * WIDE_NW; }
+
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.Lq <= 0) return hipSuccess;
@@ -1166,8 +1224,16 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
       // Fewer 256-query workgroups than two rounds of the 256 CUs (short sequences):
       // 128-query workgroups of 4 waves, two per CU, so the last round runs on
       // finer pieces (at full length the 8-wave form is about 7% faster).
-      const long long g8 = (long long)((a.Lq + 255) / 256) * a.heads * a.B;
-      if (g8 < 512) return launch_attn_wide<128, WIDE_NR, 1, 4>(a, st);
+      if (!attn_static_max_path(a.hd, a.Lq, a.heads, a.B, true, false))
+        return launch_attn_wide<128, WIDE_NR, 1, 4>(a, st);
+      if (a.kpart && a.fallback) {
+        // static maximum, then the running-maximum kernel on the workgroups it flagged
+        hipError_t e = launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW, true>(a, st);
+        if (e != hipSuccess) return e;
+        AttnArgs b = a;
+        b.only = a.fallback;
+        return launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW>(b, st);
+      }
       return launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW>(a, st);
     }
   }

@@ -1211,6 +1211,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         }
       }
     } else {
+      // k rows of a packing GEMM with kpart: each (row, head) of a 128-column slab sits in 16
+      // consecutive lanes (one 8-column chunk each); a thread keeps the largest |k|^2 it saw
+      constexpr bool KMAX = EPI == EPI_PACK && SW == 128 && NT % 16 == 0;
+      const bool kmax_on = KMAX && g.kpart && sec == 1;
+      float ksq[KMAX ? IT : 1];  // this thread's chunk of each item's row: sum of 8 squares
+#pragma unroll
+      for (int it = 0; it < (KMAX ? IT : 1); ++it) ksq[it] = 0.f;
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int idx = tid + it * NT;
@@ -1364,6 +1371,34 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             pack8(c, v);
             T* base = reinterpret_cast<T*>(sec == 0 ? g.q : g.k);
             c.store(base + rowidx * g.hd + e0);
+            if constexpr (KMAX) {
+              if (kmax_on) {
+                // |k|^2 of the row before its rounding to bf16, this chunk's share (rounding
+                // to nearest moves a norm by at most 2^-9 of itself; the attention's margin
+                // covers that)
+                float sq = 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) sq = __builtin_fmaf(v[u], v[u], sq);
+                ksq[it] = sq;
+              }
+            }
+          }
+        }
+      }
+      if constexpr (KMAX) {
+        if (kmax_on) {
+          // row sums over each row's 16 lanes (skipped rows hold zeros), the largest of this
+          // thread's rows, the wave's four row groups, then one partial maximum per wave (no
+          // atomics: the attention kernel reduces the partials of its (batch item, head))
+          float kacc = 0.f;
+#pragma unroll
+          for (int it = 0; it < IT; ++it) kacc = __builtin_elementwise_maximum(kacc, row16_sum(ksq[it]));
+          kacc = __builtin_elementwise_maximum(kacc, __shfl_xor(kacc, 16, 64));
+          kacc = __builtin_elementwise_maximum(kacc, __shfl_xor(kacc, 32, 64));
+          if (lane == 0) {
+            const int hh = (nbase - g.nq) / g.hd;
+            const int b = m0 / g.c_rpb, mt = (m0 - b * g.c_rpb) / BM;
+            g.kpart[((long long)b * g.heads + hh) * g.kpart_n + mt * C::NW + wave] = kacc;
           }
         }
       }
@@ -1385,6 +1420,10 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   static_assert(OCC * C::LDS_BYTES <= 160 * 1024, "occupancy exceeds the LDS");
   if (g.N % BN != 0) return hipErrorInvalidValue;
   if ((LOADER == LOAD_PLAIN || LOADER == LOAD_FP8 || LOADER == LOAD_CONV) && g.K % C::BK != 0)
+    return hipErrorInvalidValue;
+  // the k-row norms need one 128-wide head per 128-column slab, and tiles inside one batch item
+  if (g.kpart && !(EPI == EPI_PACK && C::SW == 128 && C::NT % 16 == 0 && g.hd == 128 && g.c_rpb % BM == 0 &&
+                   g.nq % 128 == 0 && g.kpart_n == g.c_rpb / BM * C::NW))
     return hipErrorInvalidValue;
   auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, RB, OCC, LOADER, EPI, MI>;
   static bool attr_set = false;
