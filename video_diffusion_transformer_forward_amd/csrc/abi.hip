@@ -396,6 +396,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     if (static_max) {
       g.kpart = kpart;
       g.kpart_n = kpart_n;
+      g.q_scale = scale_log2;  // q leaves the epilogue in base-2 score units
     }
     if (d.qk8) {
       // e4m3 q / k take the first half of their bf16 regions, the scale bytes follow
@@ -414,6 +415,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
       a.kpart = kpart;
       a.kpart_n = kpart_n;
       a.fallback = aflag;
+      a.scale_log2 = 1.0f;  // q carries log2(e)/sqrt(hd) already
     }
     if (d.qk8) {
       a.qk8 = 1;

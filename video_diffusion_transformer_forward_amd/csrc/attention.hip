@@ -350,7 +350,9 @@ __device__ __forceinline__ void att_barrier_lds() {
 // SM (static maximum): every query's exponent offset is fixed before the key sweep at
 // m_q = |q| max_k |k| (by Cauchy-Schwarz no score exceeds it, so every probability is at
 // most 1), which removes the per-tile row maxima, the running-max update and the
-// rescaling of the accumulators.  The result is the same softmax; only its scale
+// rescaling of the accumulators.  q arrives multiplied by log2(e)/sqrt(d) (scale_log2 is 1),
+// so the scores are in base-2 units, and the score accumulators start at -m_q: a
+// probability is exp2 of the accumulator, with no per-score multiply-add.  The result is the same softmax; only its scale
 // differs, and exactness needs the largest probability of a row to stay far above
 // the smallest normal float: a workgroup with a row sum below 2^-64 (the offset
 // overshot the true maximum by more than 64 in base 2) flags itself in a.fallback (one
@@ -453,6 +455,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
       __builtin_amdgcn_global_load_lds(src + vdo[i], (lds_void*)(dst + (wave * Cfg::V_DMA + i) * 1024), 16, 0, 0);
   };
 
+  f32x16 sinit[QB];  // initial score accumulators (set below, once the offsets are known)
   // S^T of one 32-key block kb of the K tile in stage kst, for both query blocks
   auto scores = [&](f32x16 (&s)[QB][2], int kst, int kb) {
     const unsigned char* kbase = smem_raw + kst * Cfg::KT_B + kb * KBLK_B;
@@ -462,10 +465,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
       ka.load(kbase + koff[st]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if (st == 0) {
-          const f32x16 zero = {};
-          s[qb][kb] = zero;
-        }
+        if (st == 0) s[qb][kb] = sinit[qb];
         mma32(s[qb][kb], ka, qf[qb][st]);
       }
     }
@@ -532,6 +532,12 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
       m[qb] = sqrtf(q2 * k2) * (1.0f + 1.0f / 256.0f);
     }
   }
+  // score accumulators start at 0, or (static offset, q pre-scaled by log2(e)/sqrt(d)) at -m_q,
+  // so that the probability is exp2 of the accumulator itself
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sinit[qb][r] = SM ? -m[qb] : 0.f;
 
   // Lazy running max: a query's max moves only when its tile max exceeds it by
   // more than 2^8; its sum is then scaled by alpha at once, the accumulators
@@ -571,7 +577,8 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * half + e], c, nmc));
+          p[e] = SM ? __builtin_amdgcn_exp2f(s[qb][kb][8 * half + e])
+                    : __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * half + e], c, nmc));
           l[qb] += p[e];
         }
         pack8(pf[qb][2 * kb + half], p);
@@ -671,10 +678,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
       for (int qb = 0; qb < QB; ++qb) {
         if (i < 16) {
           const int kb = i / 8, st = i % 8;
-          if (st == 0) {
-            const f32x16 zero = {};
-            S[qb][kb] = zero;
-          }
+          if (st == 0) S[qb][kb] = sinit[qb];
           mma32(S[qb][kb], rf[i], qf[qb][st]);
         } else {
           const int u = (i - 16) / 4, db = (i - 16) % 4;
@@ -687,7 +691,8 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
           for (int e = 2 * i; e < 2 * i + 2; ++e) {
-            pbuf[qb][e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][1][e], c, nmc[qb]));
+            pbuf[qb][e % 8] = SM ? __builtin_amdgcn_exp2f(S[qb][1][e])
+                                 : __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][1][e], c, nmc[qb]));
             l[qb] += pbuf[qb][e % 8];
           }
           if (i % 4 == 3) {
@@ -732,7 +737,8 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
           for (int e = 2 * (i - 24); e < 2 * (i - 24) + 2; ++e) {
-            pbuf[qb][e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][0][e], c, nmc[qb]));
+            pbuf[qb][e % 8] = SM ? __builtin_amdgcn_exp2f(S[qb][0][e])
+                                 : __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][0][e], c, nmc[qb]));
             l[qb] += pbuf[qb][e % 8];
           }
           if (i % 4 == 3) {
@@ -1226,7 +1232,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
       // finer pieces (at full length the 8-wave form is about 7% faster).
       if (!attn_static_max_path(a.hd, a.Lq, a.heads, a.B, true, false))
         return launch_attn_wide<128, WIDE_NR, 1, 4>(a, st);
-      if (a.kpart && a.fallback) {
+      if (a.kpart && a.fallback && a.scale_log2 == 1.0f) {
         // static maximum, then the running-maximum kernel on the workgroups it flagged
         hipError_t e = launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW, true>(a, st);
         if (e != hipSuccess) return e;

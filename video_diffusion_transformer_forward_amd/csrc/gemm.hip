@@ -1353,6 +1353,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             }
           }
           const long long rowidx = ((long long)b * g.heads + hh) * g.Lp + t;
+          if (EPI == EPI_PACK && sec == 0 && g.q_scale != 1.0f) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] *= g.q_scale;
+          }
           if constexpr (EPI == EPI_PACK8) {
             // e4m3 with one power-of-two scale per (token, head), stored as the
             // byte e + 127 (e8_exponent); max|row| gathers over the 16 lanes of the head

@@ -85,6 +85,7 @@ struct GemmArgs {
   // (tile = the 256-row tile's index inside batch item b; kpart_n = tiles per item x waves)
   float* kpart = nullptr;
   int kpart_n = 0;
+  float q_scale = 1.0f;  // EPI_PACK (bf16): the q section is multiplied by this after RoPE
 };
 
 template <typename T> hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st);
@@ -112,7 +113,8 @@ struct AttnArgs {
   // maxima of |k|^2 over the keys, as the QKV epilogue writes them) and fallback
   // ([attn_wide_flags] ints, any contents) the probabilities take the static offset
   // |q| max|k| (no running maximum); the workgroups that flag an under-flowing row are then
-  // recomputed with the running maximum
+  // recomputed with the running maximum.  This path expects q already multiplied by
+  // log2(e)/sqrt(hd) and scale_log2 == 1
   const float* kpart = nullptr;
   int kpart_n = 0;
   int* fallback = nullptr;
