@@ -48,19 +48,21 @@ def test_self_attention_ragged_lengths(L, qk8):
     assert err <= TOL["bf16"]
 
 
-def test_self_attention_static_offset_fallback():
+@pytest.mark.parametrize("qk8", [False, True], ids=["bf16", "qk8"])
+def test_self_attention_static_offset_fallback(qk8):
     """The 256-query bf16 kernel offsets every exponent by |q| max_k |k|, which bounds the scores
     from above; when that bound overshoots a row's largest score by more than 64 in base 2 the
     workgroup is recomputed with the running maximum.  Here one token's key in head 0 carries a
     component of about 800 along feature d-1 (the slowest-turning RoPE pair): the bound of
     every head-0 query is then hundreds of powers of two above its scores, so all of head 0 takes
     the recomputation, while the other heads stay on the static offset.  Half of the head-0
-    queries (q_{d-1} > 0) are dominated by that key, the others ignore it."""
+    queries (q_{d-1} > 0) are dominated by that key, the others ignore it.  Both the bf16 kernel
+    and the 8-bit-score kernel (against the oracle's 8-bit reading) take this path."""
     f, h, w_ = GRIDS[11000]
     base = S.get_config("wan13b_block")
-    cfg = base.with_(name="wan13b_L11000_fb", seed_base=77, frames=f, height=2 * h, width=2 * w_)
+    cfg = base.with_(name="wan13b_L11000_fb", seed_base=77, frames=f, height=2 * h, width=2 * w_, qk8=qk8)
     L = cfg.seq_len
-    announce(f"self-attention static-offset fallback L={L}")
+    announce(f"self-attention static-offset fallback L={L} qk8={qk8}")
     w, x, mod, ctx = block_case(cfg)
     w, mod = self_attention_only(cfg, w, mod)
     D, d = cfg.dim, cfg.head_dim
@@ -72,7 +74,7 @@ def test_self_attention_static_offset_fallback():
     rows = sorted(set(sample_rows(L, 16, seed=5) + [tok, tok + 1]))
     got = gpu_block(cfg, w, x, mod, ctx)
     assert np.all(np.isfinite(got))
-    ref = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, 0, rows=rows)
+    ref = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, 0, rows=rows, qk8=qk8)
     err = inc_err(got[:, rows], ref, x[:, rows])
-    print(f"L={L} planted large-norm key: rel err {err:.3e} over {len(rows)} rows")
+    print(f"L={L} planted large-norm key qk8={qk8}: rel err {err:.3e} over {len(rows)} rows")
     assert err <= TOL["bf16"]

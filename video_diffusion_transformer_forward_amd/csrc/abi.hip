@@ -396,7 +396,9 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     if (static_max) {
       g.kpart = kpart;
       g.kpart_n = kpart_n;
-      g.q_scale = scale_log2;  // q leaves the epilogue in base-2 score units
+      // bf16 q leaves the epilogue in base-2 score units; 8-bit q keeps its projected values
+      // (its e4m3 rounding is taken on q as projected), the attention scales its scores
+      if (!d.qk8) g.q_scale = scale_log2;
     }
     if (d.qk8) {
       // e4m3 q / k take the first half of their bf16 regions, the scale bytes follow
@@ -415,7 +417,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
       a.kpart = kpart;
       a.kpart_n = kpart_n;
       a.fallback = aflag;
-      a.scale_log2 = 1.0f;  // q carries log2(e)/sqrt(hd) already
+      if (!d.qk8) a.scale_log2 = 1.0f;  // q carries log2(e)/sqrt(hd) already
     }
     if (d.qk8) {
       a.qk8 = 1;

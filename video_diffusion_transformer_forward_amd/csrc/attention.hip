@@ -841,7 +841,13 @@ __device__ __forceinline__ void mma8(f32x16& acc, const i32x8& k, const i32x8& q
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k, q, acc, 0, 0, 0, kscale, 0, qscale);
 }
 
-template <int NR, int NW>
+// SM: the static offset of the bf16 kernel above, with the dequantised q (e4m3 bytes times
+// their power-of-two scale) and max |k| taken before the e4m3 rounding of k, whose relative
+// error (at most 2^-4 per element, far less on the norm of a 128-wide row scaled to its
+// maximum) the factor 1 + 2^-3 covers.  q is rounded to e4m3 as projected (a prior scaling
+// by log2(e)/sqrt(d) would change its rounded bytes), so the offset is in score units and
+// each probability is exp2(c S) with S seeded at -m_q: one multiply per score.
+template <int NR, int NW, bool SM = false>
 __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
   using T = bf16;
   using Cfg = Wide8Cfg<NR, NW>;
@@ -865,6 +871,13 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
   const int bh = id / nqt;
   const int b = bh / a.heads;
   const int h = bh - b * a.heads;
+  // second pass after the static-offset kernel: only the workgroups it flagged (one flag per wave)
+  if (!SM && a.only) {
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= a.only[id * NW + w];
+    if (any == 0) return;
+  }
   const int q0 = qt * BMQ + wave * 32;
   const float c = a.scale_log2;
   const int Lk = a.Lk[0];
@@ -940,6 +953,30 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = -INFINITY, l = 0.f, alpha = 1.f;
+  if constexpr (SM) {
+    float k2 = 0.f;
+    for (int i = lane; i < a.kpart_n; i += 64) k2 = __builtin_elementwise_maximum(k2, a.kpart[(long long)bh * a.kpart_n + i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) k2 = __builtin_elementwise_maximum(k2, __shfl_xor(k2, o, 64));
+    // |q|^2 of the dequantised query: this lane's 64 e4m3 bytes, the other half from lane ^ 32
+    float q2 = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int word = qf[s][w];
+        const float e0 = __builtin_amdgcn_cvt_f32_fp8(word, 0), e1 = __builtin_amdgcn_cvt_f32_fp8(word, 1);
+        const float e2 = __builtin_amdgcn_cvt_f32_fp8(word, 2), e3 = __builtin_amdgcn_cvt_f32_fp8(word, 3);
+        q2 = __builtin_fmaf(e0, e0, __builtin_fmaf(e1, e1, __builtin_fmaf(e2, e2, __builtin_fmaf(e3, e3, q2))));
+      }
+    q2 += __shfl_xor(q2, 32, 64);
+    const float qs = __uint_as_float((unsigned)qsc << 23);  // 2^(qsc - 127)
+    m = sqrtf(q2 * k2) * qs * (1.0f + 1.0f / 8.0f);
+  }
+  // score accumulators start at 0, or (static offset, in score units) at -m_q
+  f32x16 sinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sinit[r] = SM ? -m : 0.f;
 
   // lazy running max, as in the bf16 kernel
   auto new_max = [&](float mx) {
@@ -972,9 +1009,8 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
   att_wait_vmcnt<0>();
   __syncthreads();
   {
-    const f32x16 zero = {};
-    S0 = zero;
-    S1[0] = zero;
+    S0 = sinit;
+    S1[0] = sinit;
     const int ks0 = kscale(0, 0), ks1 = kscale(0, 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -985,17 +1021,19 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
       mask_block(S0, 0, 0);
       mask_block(S1[0], 0, 1);
     }
-    float v = -INFINITY;
+    if constexpr (!SM) {
+      float v = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v = __builtin_elementwise_maximum(v, __builtin_elementwise_maximum(S0[r], S1[0][r]));
-    new_max(__builtin_elementwise_maximum(v, __shfl_xor(v, 32, 64)));
+      for (int r = 0; r < 16; ++r) v = __builtin_elementwise_maximum(v, __builtin_elementwise_maximum(S0[r], S1[0][r]));
+      new_max(__builtin_elementwise_maximum(v, __shfl_xor(v, 32, 64)));
+    }
     const float nmc = -m * c;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[8 * half + e], c, nmc));
+        p[e] = SM ? __builtin_amdgcn_exp2f(S0[8 * half + e] * c) : __builtin_amdgcn_exp2f(__builtin_fmaf(S0[8 * half + e], c, nmc));
         l += p[e];
       }
       pack8(pf[half], p);
@@ -1041,8 +1079,7 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
       if (i < 4) {
         const int kb = i / 2, s = i % 2;
         if (s == 0) {
-          const f32x16 zero = {};
-          if (kb == 0) S0 = zero; else Sn = zero;
+          if (kb == 0) S0 = sinit; else Sn = sinit;
         }
         if (kb == 0) mma8(S0, kf[i], qf[s], ks0, qsc);
         else mma8(Sn, kf[i], qf[s], ks1, qsc);
@@ -1054,7 +1091,7 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
         // probabilities of tile t, keys 32..63: elements 2i, 2i+1 of Sc
 #pragma unroll
         for (int e = 2 * i; e < 2 * i + 2; ++e) {
-          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[e], c, nmc));
+          pbuf[e % 8] = SM ? __builtin_amdgcn_exp2f(Sc[e] * c) : __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[e], c, nmc));
           l += pbuf[e % 8];
         }
         if (i % 4 == 3) {
@@ -1066,20 +1103,22 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
         const int kb = (i - 8) / 2, k = (i - 8) % 2;
         f32x16& Sb = kb == 0 ? S0 : Sn;
         if (k == 0 && mask_next) mask_block(Sb, t + 1, kb);
+        if constexpr (!SM) {
 #pragma unroll
-        for (int r = 8 * k; r < 8 * k + 8; r += 2)
-          vmax = __builtin_elementwise_maximum(vmax, __builtin_elementwise_maximum(Sb[r], Sb[r + 1]));
-        asm volatile("" : "+v"(vmax));
-        if (i == 11) {
-          moved = new_max(__builtin_elementwise_maximum(vmax, __shfl_xor(vmax, 32, 64)));
-          nmc = -m * c;
-          asm volatile("" : "+v"(m), "+v"(l), "+v"(alpha), "+v"(nmc));
+          for (int r = 8 * k; r < 8 * k + 8; r += 2)
+            vmax = __builtin_elementwise_maximum(vmax, __builtin_elementwise_maximum(Sb[r], Sb[r + 1]));
+          asm volatile("" : "+v"(vmax));
+          if (i == 11) {
+            moved = new_max(__builtin_elementwise_maximum(vmax, __shfl_xor(vmax, 32, 64)));
+            nmc = -m * c;
+            asm volatile("" : "+v"(m), "+v"(l), "+v"(alpha), "+v"(nmc));
+          }
         }
       } else {
         // probabilities of tile t+1, keys 0..31: elements 2(i-12), +1 of S0
 #pragma unroll
         for (int e = 2 * (i - 12); e < 2 * (i - 12) + 2; ++e) {
-          pbuf[e % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], c, nmc));
+          pbuf[e % 8] = SM ? __builtin_amdgcn_exp2f(S0[e] * c) : __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], c, nmc));
           l += pbuf[e % 8];
         }
         if (i % 4 == 3) {
@@ -1104,6 +1143,10 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
   }
   att_wait_vmcnt<0>();
   __syncthreads();
+  if constexpr (SM) {
+    const int flag = __ballot((l + __shfl_xor(l, 32, 64)) < 0x1p-64f) != 0 ? 1 : 0;
+    if (lane == 0) a.fallback[id * NW + wave] = flag;
+  }
 
   // ---- epilogue: normalise, stage the wave's 32 rows in LDS as [query][d], 16-byte row stores
   constexpr int HC = HD / 8;
@@ -1145,9 +1188,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && QB == 1) ? 2 : 1) void attn_se
   attn_wide_body<HD, NR, QB, NW, SM>(a);
 }
 // bf16 self-attention with 8-bit scores: 8 waves of 32 queries, one workgroup per CU
-template <int NR, int NW>
+template <int NR, int NW, bool SM>
 __global__ __launch_bounds__(64 * NW, 1) void attn_self_qk8_kernel(const AttnArgs a) {
-  attn_wide8_body<NR, NW>(a);
+  attn_wide8_body<NR, NW, SM>(a);
 }
 // image + text sources keep a second accumulator: one workgroup per CU
 template <typename T, int HD>
@@ -1192,10 +1235,10 @@ hipError_t launch_attn_wide(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int NR, int NW>
+template <int NR, int NW, bool SM = false>
 hipError_t launch_attn_qk8(const AttnArgs& a, hipStream_t st) {
   using Cfg = Wide8Cfg<NR, NW>;
-  auto kern = attn_self_qk8_kernel<NR, NW>;
+  auto kern = attn_self_qk8_kernel<NR, NW, SM>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1210,8 +1253,10 @@ hipError_t launch_attn_qk8(const AttnArgs& a, hipStream_t st) {
 }
 
 bool attn_static_max_path(int hd, int Lq, int heads, int B, bool bf16, bool qk8) {
+  // the 8-bit-score kernel always runs 256-query workgroups
+  if (qk8) return bf16 && hd == 128;
   const long long g8 = (long long)((Lq + 255) / 256) * heads * B;
-  return bf16 && !qk8 && hd == 128 && g8 >= 512;
+  return bf16 && hd == 128 && g8 >= 512;
 }
 int attn_wide_flags(int Lq, int heads, int B) { return ((Lq + 255) / 256) * heads * B * WIDE_NW; }
 
@@ -1223,7 +1268,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     if (sizeof(T) != 2 || a.hd != 128 || a.nsrc != 1 || !a.qs || !a.ks || a.Lk[0] < 1 || a.Lkp[0] % ATT_BN != 0 ||
         a.Lkp[0] < a.Lk[0])
       return hipErrorInvalidValue;
-    if constexpr (sizeof(T) == 2) return launch_attn_qk8<2, 8>(a, st);
+    if constexpr (sizeof(T) == 2) {
+      if (a.kpart && a.fallback) {
+        // static offset, then the running-maximum kernel on the workgroups it flagged
+        hipError_t e = launch_attn_qk8<2, 8, true>(a, st);
+        if (e != hipSuccess) return e;
+        AttnArgs b = a;
+        b.only = a.fallback;
+        return launch_attn_qk8<2, 8>(b, st);
+      }
+      return launch_attn_qk8<2, 8>(a, st);
+    }
   }
   if constexpr (sizeof(T) == 2) {
     if (a.hd == 128 && a.nsrc == 1 && a.self) {

@@ -1213,7 +1213,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     } else {
       // k rows of a packing GEMM with kpart: each (row, head) of a 128-column slab sits in 16
       // consecutive lanes (one 8-column chunk each); a thread keeps the largest |k|^2 it saw
-      constexpr bool KMAX = EPI == EPI_PACK && SW == 128 && NT % 16 == 0;
+      constexpr bool KMAX = (EPI == EPI_PACK || EPI == EPI_PACK8) && SW == 128 && NT % 16 == 0;
       const bool kmax_on = KMAX && g.kpart && sec == 1;
       float ksq[KMAX ? IT : 1];  // this thread's chunk of each item's row: sum of 8 squares
 #pragma unroll
@@ -1353,7 +1353,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             }
           }
           const long long rowidx = ((long long)b * g.heads + hh) * g.Lp + t;
-          if (EPI == EPI_PACK && sec == 0 && g.q_scale != 1.0f) {
+          if (sec == 0 && g.q_scale != 1.0f) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] *= g.q_scale;
           }
@@ -1370,6 +1370,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             unsigned char* base = reinterpret_cast<unsigned char*>(sec == 0 ? g.q : g.k);
             *reinterpret_cast<uint2*>(base + rowidx * g.hd + e0) = e4m3_pack8(v, inv);
             if (e0 == 0) (sec == 0 ? g.qs : g.ks)[rowidx] = (unsigned char)(ex + 127);
+            if constexpr (KMAX) {
+              if (kmax_on) {
+                // |k|^2 before the e4m3 rounding, this chunk's share (the attention's margin
+                // covers the rounding)
+                float sq = 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) sq = __builtin_fmaf(v[u], v[u], sq);
+                ksq[it] = sq;
+              }
+            }
           } else {
             Chunk<T> c;
             pack8(c, v);
@@ -1426,7 +1436,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   if ((LOADER == LOAD_PLAIN || LOADER == LOAD_FP8 || LOADER == LOAD_CONV) && g.K % C::BK != 0)
     return hipErrorInvalidValue;
   // the k-row norms need one 128-wide head per 128-column slab, and tiles inside one batch item
-  if (g.kpart && !(EPI == EPI_PACK && C::SW == 128 && C::NT % 16 == 0 && g.hd == 128 && g.c_rpb % BM == 0 &&
+  if (g.kpart && !((EPI == EPI_PACK || EPI == EPI_PACK8) && C::SW == 128 && C::NT % 16 == 0 && g.hd == 128 && g.c_rpb % BM == 0 &&
                    g.nq % 128 == 0 && g.kpart_n == g.c_rpb / BM * C::NW))
     return hipErrorInvalidValue;
   auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, RB, OCC, LOADER, EPI, MI>;

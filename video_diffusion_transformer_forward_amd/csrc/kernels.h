@@ -80,12 +80,12 @@ struct GemmArgs {
   int nq = 0, nk = 0;
   int heads = 1, hd = 128, Lp = 64;
   const float2* rope = nullptr;  // per-token (cos, sin) table [token][hd/2], or NULL for no rotation
-  // EPI_PACK with 128-wide heads: when set, every wave of a k-section tile writes the largest
+  // EPI_PACK / EPI_PACK8 with 128-wide heads: when set, every wave of a k-section tile writes the largest
   // |k|^2 of the stored k rows it handled to kpart[(b * heads + h) * kpart_n + tile * waves + wave]
   // (tile = the 256-row tile's index inside batch item b; kpart_n = tiles per item x waves)
   float* kpart = nullptr;
   int kpart_n = 0;
-  float q_scale = 1.0f;  // EPI_PACK (bf16): the q section is multiplied by this after RoPE
+  float q_scale = 1.0f;  // EPI_PACK / EPI_PACK8: the q section is multiplied by this after RoPE
 };
 
 template <typename T> hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st);
@@ -113,15 +113,17 @@ struct AttnArgs {
   // maxima of |k|^2 over the keys, as the QKV epilogue writes them) and fallback
   // ([attn_wide_flags] ints, any contents) the probabilities take the static offset
   // |q| max|k| (no running maximum); the workgroups that flag an under-flowing row are then
-  // recomputed with the running maximum.  This path expects q already multiplied by
-  // log2(e)/sqrt(hd) and scale_log2 == 1
+  // recomputed with the running maximum.  The bf16 kernel takes this path with q already
+  // multiplied by log2(e)/sqrt(hd) and scale_log2 == 1; the 8-bit-score kernel with q as
+  // projected and scale_log2 == log2(e)/sqrt(hd)
   const float* kpart = nullptr;
   int kpart_n = 0;
   int* fallback = nullptr;
   const int* only = nullptr;  // set internally: run only the workgroups flagged here
 };
 template <typename T> hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
-// whether launch_attention takes the 256-query (static-maximum capable) self-attention path
+// whether launch_attention takes a 256-query (static-maximum capable) self-attention path: the
+// bf16 kernel at full length, or the 8-bit-score kernel
 bool attn_static_max_path(int hd, int Lq, int heads, int B, bool bf16, bool qk8);
 int attn_wide_flags(int Lq, int heads, int B);
 
