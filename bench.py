@@ -34,11 +34,11 @@ CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 # scaled by known/counted bytes of the 1 GiB calibration copy in the same run.  Valid only for the kernel
 # sources they were taken on (checked by hash).
 ATTN_COUNTERS = {
-    "fetch_kib": 885097.55 + 117.00, "fetch_scale": 1048576 / 524303.00,
-    "write_kib": 196656.01 + 0.0, "write_scale": 1048576 / 1048576.0,
+    "fetch_kib": 885077.52 + 111.50, "fetch_scale": 1048576 / 524302.69,
+    "write_kib": 196656.03 + 0.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "2bd4f4bcfd35e4ffa924fdad6c9471213fa3b9aab583f018452af1c9dee7b2b9",
+    "sha256": "c3439b2df13e2096269c697a7fed2e835d1ce11c8f5af8ee15fd1edda1c1fd2e",
 }
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 
