@@ -437,22 +437,28 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
     const int r = P / 8;
     vdo[i] = (unsigned)(r * Lkp + att_swz<T, 8>(r, P % 8) * 8) * 2u;
   }
-  const unsigned char* Kg = reinterpret_cast<const unsigned char*>(a.k[0]) + (long long)bh * Lkp * HD * 2;
-  const unsigned char* Vg = reinterpret_cast<const unsigned char*>(a.vt[0]) + (long long)bh * HD * Lkp * 2;
+  // The copies go through buffer resources based at this (batch item, head)'s K and V^T (the
+  // tile offset in the scalar offset).  Global-address LDS copies would count as both a memory
+  // and an LDS access, and every later wait for an LDS operand read would then have to drain
+  // all reads in flight (lgkmcnt(0)) instead of only the one it needs.
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const unsigned char*>(a.k[0]) + (long long)bh * Lkp * HD * 2), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const unsigned char*>(a.vt[0]) + (long long)bh * HD * Lkp * 2), (short)0, -1, 0x00020000);
 
   auto issue_k = [&](int j, int stage) {
-    const unsigned char* src = Kg + (long long)j * Cfg::KT_B;
     unsigned char* dst = smem_raw + stage * Cfg::KT_B;
 #pragma unroll
     for (int i = 0; i < Cfg::K_DMA; ++i)
-      __builtin_amdgcn_global_load_lds(src + kdo[i], (lds_void*)(dst + (wave * Cfg::K_DMA + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + (wave * Cfg::K_DMA + i) * 1024), 16, kdo[i],
+                                               j * Cfg::KT_B, 0, 0);
   };
   auto issue_v = [&](int j, int stage) {
-    const unsigned char* src = Vg + (long long)j * ATT_BN * 2;
     unsigned char* dst = smem_raw + VRING + stage * Cfg::VT_B;
 #pragma unroll
     for (int i = 0; i < Cfg::V_DMA; ++i)
-      __builtin_amdgcn_global_load_lds(src + vdo[i], (lds_void*)(dst + (wave * Cfg::V_DMA + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + (wave * Cfg::V_DMA + i) * 1024), 16, vdo[i],
+                                               j * ATT_BN * 2, 0, 0);
   };
 
   f32x16 sinit[QB];  // initial score accumulators (set below, once the offsets are known)
@@ -923,27 +929,32 @@ __device__ __forceinline__ void attn_wide8_body(const AttnArgs& a) {
     const int r = P / 8;
     vdo[i] = (unsigned)(r * Lkp + att_swz<T, 8>(r, P % 8) * 8) * 2u;
   }
-  const unsigned char* Kg = reinterpret_cast<const unsigned char*>(a.k[0]) + (long long)bh * Lkp * HD;
-  const unsigned char* Vg = reinterpret_cast<const unsigned char*>(a.vt[0]) + (long long)bh * HD * Lkp * 2;
+  // buffer-resource copies, as in the bf16 kernel (the waits for LDS operand reads stay counted)
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const unsigned char*>(a.k[0]) + (long long)bh * Lkp * HD), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const unsigned char*>(a.vt[0]) + (long long)bh * HD * Lkp * 2), (short)0, -1, 0x00020000);
   // key scales: wave 0 copies a tile's 64 bytes (lanes past 15 repeat the last word)
-  const unsigned char* Sg = a.ks + (long long)bh * Lkp + 4 * (lane < 16 ? lane : 15);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + (long long)bh * Lkp), (short)0, -1,
+                                                                      0x00020000);
+  const unsigned sdo = 4u * (unsigned)(lane < 16 ? lane : 15);
 
   auto issue_k = [&](int j, int stage) {
-    const unsigned char* src = Kg + (long long)j * Cfg::KT_B;
     unsigned char* dst = smem_raw + stage * Cfg::KT_B;
 #pragma unroll
     for (int i = 0; i < Cfg::K_DMA; ++i)
-      __builtin_amdgcn_global_load_lds(src + kdo[i], (lds_void*)(dst + (wave * Cfg::K_DMA + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + (wave * Cfg::K_DMA + i) * 1024), 16, kdo[i],
+                                               j * Cfg::KT_B, 0, 0);
     if (wave == 0)
-      __builtin_amdgcn_global_load_lds(Sg + (long long)j * ATT_BN, (lds_void*)(smem_raw + Cfg::SRING + stage * Cfg::KS_B),
-                                       4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(smem_raw + Cfg::SRING + stage * Cfg::KS_B), 4, sdo,
+                                               j * ATT_BN, 0, 0);
   };
   auto issue_v = [&](int j, int stage) {
-    const unsigned char* src = Vg + (long long)j * ATT_BN * 2;
     unsigned char* dst = smem_raw + Cfg::VRING + stage * Cfg::VT_B;
 #pragma unroll
     for (int i = 0; i < Cfg::V_DMA; ++i)
-      __builtin_amdgcn_global_load_lds(src + vdo[i], (lds_void*)(dst + (wave * Cfg::V_DMA + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + (wave * Cfg::V_DMA + i) * 1024), 16, vdo[i],
+                                               j * ATT_BN * 2, 0, 0);
   };
   auto kscale = [&](int kst, int kb) -> int { return smem_raw[Cfg::SRING + kst * Cfg::KS_B + 32 * kb + l32]; };
 
