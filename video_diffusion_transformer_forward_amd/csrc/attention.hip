@@ -157,18 +157,23 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       vdo[i] = r * Lkp + att_swz<T, 8>(r, pc % 8) * 8 + sub * (8 / SPC);
     }
 
+    // copies through buffer resources based at this source's K and V^T of (batch item, head), so
+    // that the waits for LDS operand reads stay counted (see the 256-query kernel below)
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kp, (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vp, (short)0, -1, 0x00020000);
     auto issue = [&](int j, int stage) {
       unsigned char* kst = smem_raw + stage * STAGE_B;
-      const T* kt = Kp + (long long)j * ATT_BN * HD;
 #pragma unroll
       for (int i = 0; i < Cfg::K_DMA; ++i)
-        __builtin_amdgcn_global_load_lds(kt + kdo[i], (lds_void*)(kst + (wave * Cfg::K_DMA + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kst + (wave * Cfg::K_DMA + i) * 1024), 16,
+                                                 (unsigned)kdo[i] * (unsigned)sizeof(T),
+                                                 j * ATT_BN * HD * (int)sizeof(T), 0, 0);
       unsigned char* vst = kst + Cfg::KCH * CB;
-      const T* vtile = Vp + j * ATT_BN;
 #pragma unroll
       for (int i = 0; i < Cfg::V_DMA; ++i)
-        __builtin_amdgcn_global_load_lds(vtile + vdo[i], (lds_void*)(vst + (wave * Cfg::V_DMA + i) * 1024), 16, 0,
-                                         0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vst + (wave * Cfg::V_DMA + i) * 1024), 16,
+                                                 (unsigned)vdo[i] * (unsigned)sizeof(T), j * ATT_BN * (int)sizeof(T),
+                                                 0, 0);
     };
 
     float m = -INFINITY, l = 0.f;
