@@ -614,9 +614,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     // of tile kt the W slice of tile kt+1 goes out first, then the A slice of tile
     // kt+2, spread over the MFMA slots before the tile-end wait, which lets only
     // that A slice stay in flight.  The copies are buffer loads (one descriptor per
-    // operand based at the tile's first row, 32-bit lane offsets, the k offset as
-    // the scalar offset: no vector ALU per refill), except the convolution's A
-    // operand, whose per-tap offsets go onto 64-bit lane addresses.
+    // operand based at the tile's first row, 32-bit lane offsets, the k offset (for
+    // the convolution, the tap offset plus the k offset) as the scalar offset: no
+    // vector ALU per refill).  Global-address LDS copies would also make every wait
+    // for a fragment read drain all LDS reads in flight.
     // The tile runs as KS k steps of TM*TN slots, one MFMA each, closed by a
     // scheduling barrier: a step reads the fragments of the next step in its first
     // TM+TN slots; the last step waits and synchronises after SYNC_SLOT + 1 MFMAs
@@ -630,23 +631,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int pp = lane % PPR;
     const int rlow = lane / PPR;
     // A rows: token rows of the plain loader, or output voxels of the convolution
-    // loader (its tap offsets, some negative, are added per k-tile to 64-bit
-    // addresses; a tap's channels span kpt 64-deep k-tiles)
+    // loader (the A row of a voxel is the front-top-left corner of its window in the
+    // padded buffer; later rows of a tile lie further on, and the tap offsets, added
+    // per k-tile, are non-negative; a tap's channels span kpt 64-deep k-tiles)
     const T* a_tile = reinterpret_cast<const T*>(g.A);
     unsigned a_vo[NA];  // byte offsets from the tile's first row (the host bounds them below 2^32)
-    const T* a_src[LOADER == LOAD_CONV ? NA : 1];
     const int kpt = LOADER == LOAD_CONV ? g.cv_kpt / 2 : 1;
     if constexpr (LOADER == LOAD_CONV) {
       const int hw = g.cv_h * g.cv_w;
+      auto voxel_row = [&](int r) {
+        const int tv = r / hw, rem = r - tv * hw;
+        const int hv = rem / g.cv_w, wv = rem - hv * g.cv_w;
+        return reinterpret_cast<const T*>(g.A) + (((long long)(tv + g.cv_t0) * g.cv_hp + hv) * g.cv_wp + wv) * g.lda;
+      };
+      a_tile = voxel_row(m0);
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int rt = (wave * NA + i) * RPD + rlow;
-        const int r = min(m0 + rt, g.M - 1);
-        const int tv = r / hw, rem = r - tv * hw;
-        const int hv = rem / g.cv_w, wv = rem - hv * g.cv_w;
-        a_src[i] = reinterpret_cast<const T*>(g.A) +
-                   (((long long)(tv + g.cv_t0) * g.cv_hp + hv) * g.cv_wp + wv) * g.lda + swz<RB, CPR>(rt, pp) * 8;
-        a_vo[i] = 0;
+        const T* src = voxel_row(min(m0 + rt, g.M - 1)) + swz<RB, CPR>(rt, pp) * 8;
+        a_vo[i] = (unsigned)((src - a_tile) * (long long)sizeof(T));
       }
     } else {
       {
@@ -682,7 +685,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       lds_void* dst = (lds_void*)(a_ring + (t % NST) * A_SB + (wave * NA + d) * 1024);
       if constexpr (LOADER == LOAD_CONV) {
         const int tap = t / kpt;
-        __builtin_amdgcn_global_load_lds(a_src[d] + g.tap_off[tap] + (long long)(t - tap * kpt) * BK, dst, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsa, dst, 16, a_vo[d], (int)((g.tap_off[tap] + (long long)(t - tap * kpt) * BK) * (long long)sizeof(T)), 0,
+            0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, a_vo[d], t * BK * (int)sizeof(T), 0, 0);
       }
@@ -767,48 +772,80 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int pp = lane % PPR;   // 16-byte piece within the tile row
     const int rlow = lane / PPR; // row within the instruction's RPD rows
     auto col_off = [&](int r) { return swz<RB, CPR>(r, pp / SPC) * 8 + (pp % SPC) * (8 / SPC); };
-    const T* a_src[NA];
-    const T* b_src[NB];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int rt = (wave * NA + i) * RPD + rlow;  // row within the tile
-      const int r = min(m0 + rt, g.M - 1);
-      if constexpr (LOADER == LOAD_CONV) {
-        // output voxel (t, h, w) of the chunk; the taps add their offsets per k-tile
-        const int hw = g.cv_h * g.cv_w;
+    // The plain loader copies from 64-bit lane addresses (this path also serves operands
+    // whose tile-relative offsets need more than 32 bits).  The convolution loader copies
+    // through buffer resources based at the tile's first output voxel and first W row
+    // (32-bit lane offsets, the tap and k offsets as the scalar offset; the host bounds
+    // them), so that the waits for fragment reads stay counted.
+    constexpr bool CONV = LOADER == LOAD_CONV;
+    const T* a_src[CONV ? 1 : NA];
+    const T* b_src[CONV ? 1 : NB];
+    unsigned a_vo[CONV ? NA : 1], b_vo[CONV ? NB : 1];
+    const T* a_tile = reinterpret_cast<const T*>(g.A);
+    const T* w_tile = reinterpret_cast<const T*>(g.Wt) + (long long)n0 * g.ldw;
+    if constexpr (CONV) {
+      // output voxel (t, h, w) of the chunk: the front-top-left corner of its window
+      const int hw = g.cv_h * g.cv_w;
+      auto voxel_row = [&](int r) {
         const int tv = r / hw, rem = r - tv * hw;
         const int hv = rem / g.cv_w, wv = rem - hv * g.cv_w;
-        a_src[i] = reinterpret_cast<const T*>(g.A) +
-                   (((long long)(tv + g.cv_t0) * g.cv_hp + hv) * g.cv_wp + wv) * g.lda + col_off(rt);
-      } else {
+        return reinterpret_cast<const T*>(g.A) + (((long long)(tv + g.cv_t0) * g.cv_hp + hv) * g.cv_wp + wv) * g.lda;
+      };
+      a_tile = voxel_row(m0);
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int rt = (wave * NA + i) * RPD + rlow;  // row within the tile
+        const T* src = voxel_row(min(m0 + rt, g.M - 1)) + col_off(rt);
+        a_vo[i] = (unsigned)((src - a_tile) * (long long)sizeof(T));
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int rt = (wave * NB + i) * RPD + rlow;
+        b_vo[i] = (unsigned)(((long long)rt * g.ldw + col_off(rt)) * (long long)sizeof(T));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int rt = (wave * NA + i) * RPD + rlow;  // row within the tile
+        const int r = min(m0 + rt, g.M - 1);
         const int bb = r / g.a_rpb;
         int t = r - bb * g.a_rpb;
         if (g.a_valid > 0) t = min(t, g.a_valid - 1);  // padding rows of a padded row pitch
         a_src[i] = reinterpret_cast<const T*>(g.A) + (long long)bb * g.a_bstride + (long long)t * g.lda + col_off(rt);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int rt = (wave * NB + i) * RPD + rlow;
-      b_src[i] = reinterpret_cast<const T*>(g.Wt) + (long long)(n0 + rt) * g.ldw + col_off(rt);
+      for (int i = 0; i < NB; ++i) {
+        const int rt = (wave * NB + i) * RPD + rlow;
+        b_src[i] = w_tile + (long long)rt * g.ldw + col_off(rt);
+      }
     }
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)a_tile, (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)w_tile, (short)0, -1, 0x00020000);
     auto issue = [&](int kt) {
       unsigned char* base = smem_raw + (size_t)(kt % NST) * C::STAGE * sizeof(Chunk<T>);
-      const int koff = kt * BK;
-      long long aoff = koff;
-      if constexpr (LOADER == LOAD_CONV) {
-        const int tap = kt / g.cv_kpt;
-        aoff = g.tap_off[tap] + (long long)(kt - tap * g.cv_kpt) * BK;
-      }
-#pragma unroll
-      for (int i = 0; i < NA; ++i)
-        __builtin_amdgcn_global_load_lds(a_src[i] + aoff, (lds_void*)(base + (size_t)(wave * NA + i) * 1024), 16,
-                                         0, 0);
       unsigned char* bbase = base + (size_t)BM * CPR * sizeof(Chunk<T>);
+      const int koff = kt * BK;
+      if constexpr (CONV) {
+        const int tap = kt / g.cv_kpt;
+        const int aoff = (int)((g.tap_off[tap] + (long long)(kt - tap * g.cv_kpt) * BK) * (long long)sizeof(T));
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        __builtin_amdgcn_global_load_lds(b_src[i] + koff, (lds_void*)(bbase + (size_t)(wave * NB + i) * 1024), 16,
-                                         0, 0);
+        for (int i = 0; i < NA; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(base + (size_t)(wave * NA + i) * 1024), 16, a_vo[i],
+                                                   aoff, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(bbase + (size_t)(wave * NB + i) * 1024), 16,
+                                                   b_vo[i], koff * (int)sizeof(T), 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+          __builtin_amdgcn_global_load_lds(a_src[i] + koff, (lds_void*)(base + (size_t)(wave * NA + i) * 1024), 16,
+                                           0, 0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          __builtin_amdgcn_global_load_lds(b_src[i] + koff, (lds_void*)(bbase + (size_t)(wave * NB + i) * 1024), 16,
+                                           0, 0);
+      }
     };
     static_assert(KS == 1 || KS % 2 == 0, "one or an even number of k steps per tile");
     // Every iteration first refills the stage of k-tile kt-1 (its last reads
@@ -1462,6 +1499,22 @@ inline long long split_a_span(const GemmArgs& g) {
   return items * g.a_bstride + 256LL * g.lda + g.K;
 }
 
+// The convolution loader addresses A from the tile's first output voxel: lane offsets
+// cover the frames a tile's 256 voxels can touch, the scalar offset the largest tap
+// offset plus one tap's channels; W from the tile's first row.  Both must stay below
+// 2^31 bytes, and no tap may point before the voxel's row.
+inline bool conv_offsets_fit(const GemmArgs& g) {
+  const long long hw = (long long)g.cv_h * g.cv_w;
+  const long long lane_span = (256 / hw + 2) * g.cv_hp * g.cv_wp * g.lda;
+  long long tap_max = 0;
+  for (int i = 0; i < CONV_MAX_TAPS; ++i) {
+    if (g.tap_off[i] < 0) return false;
+    tap_max = tap_max > g.tap_off[i] ? tap_max : g.tap_off[i];
+  }
+  const long long w_span = 256LL * g.ldw + g.K;
+  return (lane_span + tap_max + g.K) * 2 < (1LL << 31) && w_span * 2 < (1LL << 31);
+}
+
 template <typename T>
 bool split_offsets_fit(const GemmArgs& g) {
   const long long w_span = 256LL * g.ldw + g.K;
@@ -1529,7 +1582,7 @@ hipError_t launch_gemm(const GemmArgs& g, int loader, int epi, hipStream_t st) {
     // bf16 convolutions: whole 32-channel k-tiles per tap
     if constexpr (sizeof(T) == 2) {
       if (g.K % 32 != 0 || g.cv_kpt < 1 || g.K / 32 > g.cv_kpt * CONV_MAX_TAPS || g.K % (32 * g.cv_kpt) != 0 ||
-          g.cv_h < 1 || g.cv_w < 1)
+          g.cv_h < 1 || g.cv_w < 1 || !conv_offsets_fit(g))
         return hipErrorInvalidValue;
       if (epi == EPI_CONV) {
         // a small chunk (fewer than 128 tiles of 256 rows, e.g. one latent frame at the
