@@ -80,7 +80,7 @@ int check_shape(const wan_shape* s, Dims* d) {
 // Offsets (bytes) inside the workspace of one block run over Bb batch rows.
 struct BlockPlan {
   size_t m, r1, q, k, vt, o, ck, cvt, ik, ivt, rope, ropet;
-  // static-maximum self-attention: partial maxima of |k|^2 per (batch item, head, 256-row
+  // static-offset self-attention: partial maxima of |k|^2 per (batch item, head, 256-row
   // tile, wave of the QKV GEMM) and the per-workgroup fallback flags
   size_t kmax, aflag;
   // WAN_FP8: e4m3 LayerNorm outputs and their scales, e4m3 FFN hidden and its
@@ -375,9 +375,9 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
   // self-attention sublayer (its attention output optionally written to, or
   // taken from, the diffusion cache)
   T* a_out = attn_mode == ATTN_COMPUTE ? o : reinterpret_cast<T*>(attn_io);
-  // bf16 self-attention at full length: the static-maximum path (the QKV epilogue gathers
-  // max |k|^2 per batch row and head; flagged workgroups are recomputed)
-  const bool static_max = attn_static_max_path(d.hd, d.L, d.heads, Bb, sizeof(T) == 2, d.qk8);
+  // self-attention at full length (bf16, or 8-bit scores): the static-offset path (the QKV
+  // epilogue gathers max |k|^2 per batch row and head; flagged workgroups are recomputed)
+  const bool static_off = attn_static_offset_path(d.hd, d.L, d.heads, Bb, sizeof(T) == 2, d.qk8);
   float* kpart = reinterpret_cast<float*>(at(ws, p.kmax));
   const int kpart_n = P / 256 * 8;  // 256-row tiles per batch item x the QKV GEMM's 8 waves
   int* aflag = reinterpret_cast<int*>(at(ws, p.aflag));
@@ -393,7 +393,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     g.q = at(ws, p.q); g.k = at(ws, p.k); g.vt = at(ws, p.vt);
     g.nq = d.D; g.nk = d.D; g.heads = d.heads; g.hd = d.hd; g.Lp = d.Lp;
     g.rope = ropet;
-    if (static_max) {
+    if (static_off) {
       g.kpart = kpart;
       g.kpart_n = kpart_n;
       // bf16 q leaves the epilogue in base-2 score units; 8-bit q keeps its projected values
@@ -413,7 +413,7 @@ int run_block(const Dims& d, int Bb, const wan_block_weights* w, float* x, const
     a.q = at(ws, p.q); a.Lq = d.L; a.Lqp = d.Lp;
     a.k[0] = at(ws, p.k); a.vt[0] = at(ws, p.vt); a.Lk[0] = d.L; a.Lkp[0] = d.Lp; a.nsrc = 1; a.self = 1;
     a.o = a_out; a.B = Bb; a.heads = d.heads; a.hd = d.hd; a.scale_log2 = scale_log2;
-    if (static_max) {
+    if (static_off) {
       a.kpart = kpart;
       a.kpart_n = kpart_n;
       a.fallback = aflag;

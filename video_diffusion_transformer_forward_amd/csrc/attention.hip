@@ -352,7 +352,7 @@ __device__ __forceinline__ void att_barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
-// SM (static maximum): every query's exponent offset is fixed before the key sweep at
+// SM (static offset): every query's exponent offset is fixed before the key sweep at
 // m_q = |q| max_k |k| (by Cauchy-Schwarz no score exceeds it, so every probability is at
 // most 1), which removes the per-tile row maxima, the running-max update and the
 // rescaling of the accumulators.  q arrives multiplied by log2(e)/sqrt(d) (scale_log2 is 1),
@@ -392,7 +392,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   const int bh = id / nqt;
   const int b = bh / a.heads;
   const int h = bh - b * a.heads;
-  // second pass after the static-maximum kernel: only the workgroups it flagged (one flag per wave)
+  // second pass after the static-offset kernel: only the workgroups it flagged (one flag per wave)
   if (!SM && a.only) {
     int any = 0;
 #pragma unroll
@@ -1268,7 +1268,7 @@ hipError_t launch_attn_qk8(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-bool attn_static_max_path(int hd, int Lq, int heads, int B, bool bf16, bool qk8) {
+bool attn_static_offset_path(int hd, int Lq, int heads, int B, bool bf16, bool qk8) {
   // the 8-bit-score kernel always runs 256-query workgroups
   if (qk8) return bf16 && hd == 128;
   const long long g8 = (long long)((Lq + 255) / 256) * heads * B;
@@ -1301,10 +1301,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
       // Fewer 256-query workgroups than two rounds of the 256 CUs (short sequences):
       // 128-query workgroups of 4 waves, two per CU, so the last round runs on
       // finer pieces (at full length the 8-wave form is about 7% faster).
-      if (!attn_static_max_path(a.hd, a.Lq, a.heads, a.B, true, false))
+      if (!attn_static_offset_path(a.hd, a.Lq, a.heads, a.B, true, false))
         return launch_attn_wide<128, WIDE_NR, 1, 4>(a, st);
       if (a.kpart && a.fallback && a.scale_log2 == 1.0f) {
-        // static maximum, then the running-maximum kernel on the workgroups it flagged
+        // static offset, then the running-maximum kernel on the workgroups it flagged
         hipError_t e = launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW, true>(a, st);
         if (e != hipSuccess) return e;
         AttnArgs b = a;

@@ -122,9 +122,9 @@ struct AttnArgs {
   const int* only = nullptr;  // set internally: run only the workgroups flagged here
 };
 template <typename T> hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
-// whether launch_attention takes a 256-query (static-maximum capable) self-attention path: the
+// whether launch_attention takes a 256-query (static-offset capable) self-attention path: the
 // bf16 kernel at full length, or the 8-bit-score kernel
-bool attn_static_max_path(int hd, int Lq, int heads, int B, bool bf16, bool qk8);
+bool attn_static_offset_path(int hd, int Lq, int heads, int B, bool bf16, bool qk8);
 int attn_wide_flags(int Lq, int heads, int B);
 
 // out[r] = T( LN(x[r]) * (1 + scale[b]) + shift[b] ), rows of length D; shift/scale NULL -> plain LN
