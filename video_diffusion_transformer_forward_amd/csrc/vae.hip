@@ -85,6 +85,72 @@ __global__ __launch_bounds__(256) void vae_rms_silu_kernel(const bf16* __restric
   }
 }
 
+// The same for widths C = 24 G (96, 192 and 384 here): G lanes per voxel with three 8-channel
+// chunks each (chunk j G + lane, so no lane idles and a wave's loads stay contiguous), and
+// V voxels per lane group whose loads all go out before any arithmetic: one 16-byte load
+// per lane left too few bytes in flight per CU to cover the memory latency.
+template <int G, int V>
+__global__ __launch_bounds__(256) void vae_rms_silu24_kernel(const bf16* __restrict__ in, bf16* __restrict__ out,
+                                                             const float* __restrict__ g, int Cs, int n, int H,
+                                                             int W) {
+  constexpr int NC = 3, C = 24 * G;
+  const long long nvox = (long long)n * H * W;
+  const long long v0 = ((long long)blockIdx.x * (256 / G) + threadIdx.x / G) * V;
+  const int lg = threadIdx.x % G;
+  if (v0 >= nvox) return;  // a whole group of G lanes leaves together
+  long long off[V];
+  Chunk<bf16> raw[V][NC];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const long long vox = v0 + v < nvox ? v0 + v : nvox - 1;
+    const int w = (int)(vox % W);
+    const int h = (int)((vox / W) % H);
+    const int t = (int)(vox / ((long long)W * H));
+    off[v] = vox_off(t, h, w, H + 2, W + 2, Cs);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) raw[v][j].load(in + off[v] + (j * G + lg) * 8);
+  }
+  float gg[NC][8];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const float4 g0 = *reinterpret_cast<const float4*>(g + (j * G + lg) * 8);
+    const float4 g1 = *reinterpret_cast<const float4*>(g + (j * G + lg) * 8 + 4);
+    gg[j][0] = g0.x; gg[j][1] = g0.y; gg[j][2] = g0.z; gg[j][3] = g0.w;
+    gg[j][4] = g1.x; gg[j][5] = g1.y; gg[j][6] = g1.z; gg[j][7] = g1.w;
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float x[NC][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const bf16x8 b = as_bf16x8(raw[v][j].v);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x[j][u] = (float)b[u];
+        ss += x[j][u] * x[j][u];
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = 1.0f / sqrtf(ss / C + VAE_RMS_EPS);
+    if (v0 + v < nvox) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        float y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float r = x[j][u] * inv * gg[j][u];
+          y[u] = r * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(r * -1.4426950408889634f));
+        }
+        Chunk<bf16> c;
+        pack8(c, y);
+        c.store(out + off[v] + (j * G + lg) * 8);
+      }
+    }
+  }
+}
+
 // out (2H x 2W) frame t = nearest doubling of in (H x W) frame t, 16-byte chunks
 __global__ __launch_bounds__(256) void vae_up_space_kernel(const bf16* __restrict__ in, bf16* __restrict__ out, int n,
                                                            int H, int W, int Cs) {
@@ -165,7 +231,15 @@ hipError_t launch_vae_rms_silu(const void* in, void* out, const float* g, int C,
   if (C % 8 != 0 || C > Cs || C > 512) return hipErrorInvalidValue;
   const bf16* i = reinterpret_cast<const bf16*>(in);
   bf16* o = reinterpret_cast<bf16*>(out);
-  if (C <= 128)
+  constexpr int V = 2;  // voxels per lane group
+  const long long groups = (vox + V - 1) / V;
+  if (C == 96)
+    hipLaunchKernelGGL((vae_rms_silu24_kernel<4, V>), dim3(blocks_for(groups * 4)), dim3(256), 0, st, i, o, g, Cs, n, H, W);
+  else if (C == 192)
+    hipLaunchKernelGGL((vae_rms_silu24_kernel<8, V>), dim3(blocks_for(groups * 8)), dim3(256), 0, st, i, o, g, Cs, n, H, W);
+  else if (C == 384)
+    hipLaunchKernelGGL((vae_rms_silu24_kernel<16, V>), dim3(blocks_for(groups * 16)), dim3(256), 0, st, i, o, g, Cs, n, H, W);
+  else if (C <= 128)
     hipLaunchKernelGGL(vae_rms_silu_kernel<16>, dim3(blocks_for(vox * 16)), dim3(256), 0, st, i, o, g, C, Cs, n, H, W);
   else if (C <= 256)
     hipLaunchKernelGGL(vae_rms_silu_kernel<32>, dim3(blocks_for(vox * 32)), dim3(256), 0, st, i, o, g, C, Cs, n, H, W);
