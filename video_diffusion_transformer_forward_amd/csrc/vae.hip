@@ -154,18 +154,24 @@ __global__ __launch_bounds__(256) void vae_rms_silu24_kernel(const bf16* __restr
 // out (2H x 2W) frame t = nearest doubling of in (H x W) frame t, 16-byte chunks
 __global__ __launch_bounds__(256) void vae_up_space_kernel(const bf16* __restrict__ in, bf16* __restrict__ out, int n,
                                                            int H, int W, int Cs) {
+  // one input chunk per lane, written to its 2 x 2 output voxels (each input byte read once)
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const int cpv = Cs / 8;
-  const long long total = (long long)n * (2 * H) * (2 * W) * cpv;
+  const long long total = (long long)n * H * W * cpv;
   if (i >= total) return;
   const int c8 = (int)(i % cpv) * 8;
   const long long v = i / cpv;
-  const int w2 = (int)(v % (2 * W));
-  const int h2 = (int)((v / (2 * W)) % (2 * H));
-  const int t = (int)(v / ((long long)4 * W * H));
+  const int w = (int)(v % W);
+  const int h = (int)((v / W) % H);
+  const int t = (int)(v / ((long long)W * H));
   Chunk<bf16> c;
-  c.load(in + vox_off(t, h2 / 2, w2 / 2, H + 2, W + 2, Cs) + c8);
-  c.store(out + vox_off(t, h2, w2, 2 * H + 2, 2 * W + 2, Cs) + c8);
+  c.load(in + vox_off(t, h, w, H + 2, W + 2, Cs) + c8);
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh) {
+    bf16* o = out + vox_off(t, 2 * h + dh, 2 * w, 2 * H + 2, 2 * W + 2, Cs) + c8;
+    c.store(o);
+    c.store(o + Cs);
+  }
 }
 
 // zero the one-voxel spatial border of frames [0, frames) of a padded buffer
@@ -231,7 +237,7 @@ hipError_t launch_vae_rms_silu(const void* in, void* out, const float* g, int C,
   if (C % 8 != 0 || C > Cs || C > 512) return hipErrorInvalidValue;
   const bf16* i = reinterpret_cast<const bf16*>(in);
   bf16* o = reinterpret_cast<bf16*>(out);
-  constexpr int V = 2;  // voxels per lane group
+  constexpr int V = 4;  // voxels per lane group
   const long long groups = (vox + V - 1) / V;
   if (C == 96)
     hipLaunchKernelGGL((vae_rms_silu24_kernel<4, V>), dim3(blocks_for(groups * 4)), dim3(256), 0, st, i, o, g, Cs, n, H, W);
@@ -249,7 +255,7 @@ hipError_t launch_vae_rms_silu(const void* in, void* out, const float* g, int C,
 }
 
 hipError_t launch_vae_up_space(const void* in, void* out, int n, int H, int W, int Cs, hipStream_t st) {
-  const long long total = (long long)n * 4 * H * W * (Cs / 8);
+  const long long total = (long long)n * H * W * (Cs / 8);
   if (total <= 0) return hipSuccess;
   if (Cs % 8 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(vae_up_space_kernel, dim3(blocks_for(total)), dim3(256), 0, st, reinterpret_cast<const bf16*>(in),
