@@ -1016,6 +1016,107 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
     return;
   }
+
+  if constexpr (C::MI16 && EPI == EPI_PACK && sizeof(T) == 2 && BN / WN == 128) {
+    // q / k tiles of the 16x16 form: a lane holds four consecutive features of one token
+    // per accumulator block, i.e. two whole RoPE pairs, and each wave's 128 columns are
+    // one head.  Bias, rotation, q scale and the k-row norms are applied to the
+    // accumulators; the tile is then staged once as bf16 (like the store epilogues) and
+    // written as 16-byte pieces of head-major rows.  v^T tiles take the general path.
+    const int sec0 = n0 < g.nq ? 0 : g.nq;
+    const int sec_end = n0 < g.nq ? g.nq : g.nq + g.nk;
+    if (n0 < g.nq + g.nk && n0 + BN <= sec_end && g.hd == 128 && (n0 - sec0) % 128 == 0 &&
+        g.c_rpb % BM == 0) {
+      constexpr int SP = BN + 16;
+      static_assert((size_t)BM * SP * sizeof(T) <= C::LDS_BYTES, "bf16 staging");
+      T* stage16 = reinterpret_cast<T*>(smem_raw);
+      const bool is_k = sec0 != 0;
+      const int b = m0 / g.c_rpb, t0 = m0 - b * g.c_rpb;
+      const int valid = g.c_valid > 0 ? g.c_valid : g.c_rpb;
+      const float qsc = is_k ? 1.0f : g.q_scale;
+      const bool kmax_on = is_k && g.kpart != nullptr;
+      f32x4 bj[TC16];
+#pragma unroll
+      for (int j = 0; j < TC16; ++j) {
+        bj[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (g.bias) bj[j] = *reinterpret_cast<const f32x4*>(g.bias + n0 + brow0 + 16 * j + 4 * (lane >> 4));
+      }
+      float kacc = 0.f;  // largest |k|^2 over this lane's rows
+#pragma unroll
+      for (int i = 0; i < TR16; ++i) {
+        const int row = arow0 + 16 * i + (lane & 15);
+        const int t = t0 + row;
+        const bool live = t < valid && m0 + row < g.M;
+        // (cos, sin) of the lane's two pairs in each block; padding rows read the last token's
+        const float2* rrow = g.rope ? g.rope + (long long)min(t, valid - 1) * 64 : nullptr;
+        f32x4 cs[TC16];
+        if (rrow) {
+#pragma unroll
+          for (int j = 0; j < TC16; ++j) cs[j] = *reinterpret_cast<const f32x4*>(rrow + 8 * j + 2 * (lane >> 4));
+        }
+        float sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < TC16; ++j) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc16[i][j][e] + bj[j][e];
+          if (rrow) {
+#pragma unroll
+            for (int u = 0; u < 4; u += 2) {
+              const float u0 = v[u], u1 = v[u + 1], c = cs[j][u], s = cs[j][u + 1];
+              v[u] = u0 * c - u1 * s;
+              v[u + 1] = u0 * s + u1 * c;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= qsc;
+          if (kmax_on) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sq = __builtin_fmaf(v[e], v[e], sq);
+          }
+          *reinterpret_cast<uint2*>(stage16 + row * SP + brow0 + 16 * j + 4 * (lane >> 4)) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+        if (kmax_on) {
+          // the row's |k|^2 before the bf16 rounding (rounding to nearest moves a norm by at most
+          // 2^-9 of itself; the attention's margin covers that): four lanes of 32 features each
+          sq += __shfl_xor(sq, 16, 64);
+          sq += __shfl_xor(sq, 32, 64);
+          if (live) kacc = __builtin_elementwise_maximum(kacc, sq);
+        }
+      }
+      if (kmax_on) {
+        // one partial maximum per wave; the head's 256-row tile has 8 slots and 4 waves
+        // (wm = 0..3) cover it, so each wave fills two (the attention takes the maximum)
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) kacc = __builtin_elementwise_maximum(kacc, __shfl_xor(kacc, o, 64));
+        if (lane == 0) {
+          const int hh = (n0 + brow0 - g.nq) / 128, mt = t0 / BM;
+          float* kp = g.kpart + ((long long)b * g.heads + hh) * g.kpart_n + mt * C::NW + 2 * wm;
+          kp[0] = kacc;
+          kp[1] = kacc;
+        }
+      }
+      __syncthreads();
+      constexpr int CPR16 = BN / 8, IT16 = BM * CPR16 / NT;
+      static_assert(IT16 * NT == BM * CPR16, "whole 16-byte pieces per thread");
+      T* base = reinterpret_cast<T*>(is_k ? g.k : g.q);
+#pragma unroll
+      for (int it = 0; it < IT16; ++it) {
+        const int idx = tid + it * NT;
+        const int lrow = idx / CPR16, c8 = (idx % CPR16) * 8;
+        const int t = t0 + lrow;
+        if (t < valid && m0 + lrow < g.M) {
+          const int nsec = n0 - sec0 + c8;
+          const long long rowidx = ((long long)b * g.heads + (nsec >> 7)) * g.Lp + t;
+          Chunk<T> c;
+          c.load(stage16 + lrow * SP + c8);
+          c.store(base + rowidx * 128 + (nsec & 127));
+        }
+      }
+      return;
+    }
+  }
   // ---- epilogue.  The fp32 tile goes through LDS in column slabs; phase 2
   // walks a slab in 8-element chunks and writes 16-byte pieces.
   float* slab = reinterpret_cast<float*>(smem_raw);
