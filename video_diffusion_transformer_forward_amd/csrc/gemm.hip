@@ -1086,15 +1086,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         }
       }
       if (kmax_on) {
-        // one partial maximum per wave; the head's 256-row tile has 8 slots and 4 waves
-        // (wm = 0..3) cover it, so each wave fills two (the attention takes the maximum)
+        // one partial maximum per wave; the head's 256-row tile has 8 slots and WM waves
+        // cover it, so each wave fills 8 / WM of them (the attention takes the maximum)
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) kacc = __builtin_elementwise_maximum(kacc, __shfl_xor(kacc, o, 64));
         if (lane == 0) {
           const int hh = (n0 + brow0 - g.nq) / 128, mt = t0 / BM;
-          float* kp = g.kpart + ((long long)b * g.heads + hh) * g.kpart_n + mt * C::NW + 2 * wm;
-          kp[0] = kacc;
-          kp[1] = kacc;
+          float* kp = g.kpart + ((long long)b * g.heads + hh) * g.kpart_n + mt * 8 + (8 / WM) * wm;
+#pragma unroll
+          for (int s = 0; s < 8 / WM; ++s) kp[s] = kacc;
         }
       }
       __syncthreads();
@@ -1575,7 +1575,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
     return hipErrorInvalidValue;
   // the k-row norms need one 128-wide head per 128-column slab, and tiles inside one batch item
   if (g.kpart && !((EPI == EPI_PACK || EPI == EPI_PACK8) && C::SW == 128 && C::NT % 16 == 0 && g.hd == 128 && g.c_rpb % BM == 0 &&
-                   g.nq % 128 == 0 && g.kpart_n == g.c_rpb / BM * C::NW))
+                   g.nq % 128 == 0 && g.kpart_n == g.c_rpb / BM * (C::MI16 ? 8 : C::NW)))
     return hipErrorInvalidValue;
   auto kern = gemm_kernel<T, BM, BN, WM, WN, NST, RB, OCC, LOADER, EPI, MI>;
   static bool attr_set = false;
@@ -1640,8 +1640,10 @@ hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
         // epilogues gain 10% and 2.5% on 8 waves; a long-K residual GEMM (FFN2, K = 8960) gains
         // 6.5% on 4 waves of 128x128 (two thirds of the LDS fragment reads), while the short-K
         // residual GEMMs (K = 1536), whose epilogue dominates, stay on 8 waves of 32x32x16
-        if constexpr (EPI == EPI_PACK || EPI == EPI_STORE_GELU)
+        if constexpr (EPI == EPI_PACK)
           return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOADER, EPI, 16>(g, st);
+        if constexpr (EPI == EPI_STORE_GELU)
+          return launch_cfg<T, 256, 256, 2, 2, 3, 128, 1, LOADER, EPI, 16>(g, st);
         if constexpr (EPI == EPI_RESID)
           if (g.K >= 4096) return launch_cfg<T, 256, 256, 2, 2, 3, 128, 1, LOADER, EPI, 16>(g, st);
         return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOADER, EPI>(g, st);
