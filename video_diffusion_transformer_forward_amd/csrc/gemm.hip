@@ -1636,10 +1636,11 @@ hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
     if constexpr (LOADER == LOAD_PLAIN)
       if (g.N % 256 == 0 && g.K % 64 == 0 && big_tiles >= 128 && split_offsets_fit<T>(g)) {
         if (big_tiles < 256 && g.N % 192 == 0) return launch_cfg<T, 256, 192, 4, 2, 3, 128, 1, LOADER, EPI>(g, st);
-        // 16x16x32 MFMAs (measured on the 1.3B step shapes, same box): the packing and GELU
-        // epilogues gain 10% and 2.5% on 8 waves; a long-K residual GEMM (FFN2, K = 8960) gains
-        // 6.5% on 4 waves of 128x128 (two thirds of the LDS fragment reads), while the short-K
-        // residual GEMMs (K = 1536), whose epilogue dominates, stay on 8 waves of 32x32x16
+        // 16x16x32 MFMAs (measured on the 1.3B step shapes, same box): the packing epilogue
+        // gains 10% on 8 waves (4 waves spill its v^T staging); FFN1+GELU and a long-K residual
+        // GEMM (FFN2, K = 8960) run best on 4 waves of 128x128 (two thirds of the LDS fragment
+        // reads per MFMA), while the short-K residual GEMMs (K = 1536), whose epilogue
+        // dominates, stay on 8 waves of 32x32x16 (the 4-wave 16x16 form is 2% slower there)
         if constexpr (EPI == EPI_PACK)
           return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOADER, EPI, 16>(g, st);
         if constexpr (EPI == EPI_STORE_GELU)
