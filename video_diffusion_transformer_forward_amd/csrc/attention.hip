@@ -665,8 +665,15 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
     issue_v(min(t + NR - 1, n - 1), (ph + NR - 1) % NR);
     const unsigned char* kbase = smem_raw + kst * Cfg::KT_B;
     const unsigned char* vbase = smem_raw + VRING + vst * Cfg::VT_B;
-    // operand of slot i: K block i/8 step i%8, then V^T 16-key step (i-16)/4, d block (i-16)%4
+    // operand of slot i: K block i/8 step i%8, then V^T 16-key step (i-16)/4, d block (i-16)%4.
+    // With the static offset the slots alternate instead: K block 0, V^T keys 0..31, K block 1,
+    // V^T keys 32..63 (see the slot loop below)
     auto raddr = [&](int i) -> const unsigned char* {
+      if constexpr (SM) {
+        if ((i & 8) == 0) return kbase + (i / 16) * KBLK_B + koff[i % 8];
+        const int v = (i / 16) * 8 + (i % 8);
+        return vbase + (v % 4) * VBLK_B + voff[v / 4];
+      }
       if (i < 16) return kbase + (i / 8) * KBLK_B + koff[i % 8];
       return vbase + ((i - 16) % 4) * VBLK_B + voff[(i - 16) / 4];
     };
@@ -685,6 +692,54 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (i + AHEAD < 32) rf[i + AHEAD].load(raddr(i + AHEAD));
+      if constexpr (SM) {
+        // Static offset: no row maxima, so the only VALU work is one exp2 (and its sum) per
+        // score, spread over every slot.  The two waves of a SIMD start each tile together
+        // (one barrier per tile); with the exp2 work in half of the slots both waves issued
+        // it at once while the other half had none.
+        //   slots  0..7   S(t+1), keys 0..31    | probabilities of tile t, keys 32..63 (1st half)
+        //   slots  8..15  O += P V, keys 0..31  | probabilities of tile t, keys 32..63 (2nd half)
+        //   slots 16..23  S(t+1), keys 32..63   | masking of S(t+1) keys 0..31 at 16; probabilities of
+        //   slots 24..31  O += P V, keys 32..63 |   tile t+1, keys 0..31 (masking of its keys 32..63 at 24)
+        // S(t) keys 32..63 are read in slots 0..15, before the MFMAs of slots 16..23 overwrite
+        // them; P(t) keys 0..31 are read by slots 8..15, before slot 23 repacks them for t+1.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          if ((i & 8) == 0) {
+            const int kb = i / 16, st = i % 8;
+            if (st == 0) S[qb][kb] = sinit[qb];
+            mma32(S[qb][kb], rf[i], qf[qb][st]);
+          } else {
+            const int v = (i / 16) * 8 + (i % 8);
+            mma32(o[qb][v % 4], rf[i], pf[qb][v / 4]);
+          }
+        }
+        if ((i == 16 || i == 24) && mask_next) {
+          const int kb = i == 16 ? 0 : 1;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = (t + 1) * ATT_BN + 32 * kb + 8 * (r / 4) + 4 * g2 + (r % 4);
+              if (key >= Lk) S[qb][kb][r] = -INFINITY;
+            }
+        }
+        {
+          const int kb = i < 16 ? 1 : 0, e = i % 16;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            pbuf[qb][e % 8] = __builtin_amdgcn_exp2f(S[qb][kb][e]);
+            l[qb] += pbuf[qb][e % 8];
+            if (e % 8 == 7) {
+              const int c8 = (kb == 1 ? 2 : 0) + e / 8;
+              pack8(pf[qb][c8], pbuf[qb]);
+              asm volatile("" : "+v"(pf[qb][c8].v), "+v"(l[qb]));
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (i < 16) {
