@@ -34,11 +34,11 @@ CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 # scaled by known/counted bytes of the 1 GiB calibration copy in the same run.  Valid only for the kernel
 # sources they were taken on (checked by hash).
 ATTN_COUNTERS = {
-    "fetch_kib": 885697.32 + 109.50, "fetch_scale": 1048576 / 524302.79,
-    "write_kib": 196657.37 + 0.0, "write_scale": 1048576 / 1048576.0,
+    "fetch_kib": 885003.13 + 117.00, "fetch_scale": 1048576 / 524302.88,
+    "write_kib": 196663.41 + 0.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "086945751edbaf48da681ac0543f9d5553b5044c87e9e41363a7b9fdc29b760c",
+    "sha256": "e158d893c470c7ecfeb58628f3e2400414b8ae6a44ae575c2a19ccf86ec0554c",
 }
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 
