@@ -333,6 +333,7 @@ def main():
     ap.add_argument("--no-cache-modes", action="store_true", help="skip timing the diffusion-cache step modes")
     ap.add_argument("--no-qk8", action="store_true", help="skip timing the step in the 8-bit forms")
     ap.add_argument("--no-vae", action="store_true", help="skip timing the 480p x 81-frame VAE decode")
+    ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--vae-only", action="store_true",
                     help="time only the VAE decode and print its JSON object (for profiling runs)")
     ap.add_argument("--block-configs", default="wan13b_block,wan14b_720p_block,wan14b_i2v_block",
@@ -398,6 +399,36 @@ def main():
                                            ("cross_attention", N.KERNEL_CROSS_ATTENTION),
                                            ("gemm", N.KERNEL_GEMM), ("elementwise", N.KERNEL_ELEMENTWISE))}
     assert bool(torch.isfinite(z).all())
+
+    # the same step captured once into a HIP graph (torch.cuda.CUDAGraph on the library's
+    # launches) and replayed: the kernels are the same, the host launches and the gaps between
+    # them go; one replay from z0 is checked bit for bit against one eager step from z0
+    graph = None
+    if not args.no_graph:
+        print("[bench] graph replay", file=sys.stderr, flush=True)
+        zg = z0.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            W.denoise_step(cfg, model, zg, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws)
+        zg.copy_(z0)
+        g.replay()
+        ze = z0.clone()
+        W.denoise_step(cfg, model, ze, cond, ctx_c, ctx_n, cfg.timestep, cfg.dt, cfg.guide_scale, ws)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(zg, ze))
+        del ze
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = {"ms_per_step": round((time.perf_counter() - tg) / args.steps * 1e3, 3),
+                 "bitwise_equal_to_eager": same}
+        assert bool(torch.isfinite(zg).all())
+        del g, zg
+        torch.cuda.empty_cache()
     # the same step in the 8-bit forms (same weights): 8-bit self-attention scores
     # (WAN_BF16_QK8), and 8-bit projections on top (WAN_FP8)
     def time_variant(cfg8, reps=3):
@@ -520,6 +551,11 @@ def main():
             "self_attention_speedup": round(attn_avg / a8, 4) if a8 > 0 else None,
             "note": note + "; reduced-precision variant, not the headline value"})
         out[key] = var
+    if graph is not None:
+        graph.update({"tflops": round(flops / (graph["ms_per_step"] * 1e-3) / 1e12, 2),
+                      "note": "the timed step captured once into a HIP graph and replayed (same kernels, no "
+                              "host launches); not the headline value"})
+        out["graph_step"] = graph
     if cache_ms is not None:
         out["diffusion_cache"] = {
             "ms_per_step": cache_ms, "cache_gb": cache_gb,
