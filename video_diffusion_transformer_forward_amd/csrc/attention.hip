@@ -320,6 +320,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 constexpr int WIDE_NW = 8;  // waves per workgroup
 constexpr int WIDE_QB = 1;  // 32-query blocks per wave
 constexpr int WIDE_NR = 2;  // stages per K / V^T ring
+constexpr int WIDE_NR_SM = 3;  // the static-offset kernel: three stages, barrier at slot 24
 
 template <int HD, int NR, int QB, int NW>
 struct WideCfg {
@@ -642,6 +643,15 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
     new_max(mx);  // first tile: the max moves from -inf, sums and accumulators are still zero
   }
   probs(S, 0, pf);
+  // MB (static offset, three-stage rings): the workgroup barrier sits at slot 24 of an
+  // iteration, and slots 24..31 already read the first 8 operands of the next iteration
+  // (K_{t+2}, keys 0..31) into `carry`; here the prologue reads those of iteration 0
+  constexpr bool MB = SM && NR == 3;
+  Chunk<T> carry[8];
+  if constexpr (MB) {
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) carry[s8].load(smem_raw + 1 * Cfg::KT_B + koff[s8]);
+  }
   att_barrier_lds();  // K stage 0 is refilled by the first iteration
 
   // One iteration, entered with the scores S(t) of tile t in S and the
@@ -680,7 +690,13 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
     constexpr int AHEAD = 8;
     Chunk<T> rf[32];
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) rf[i].load(raddr(i));
+    for (int i = 0; i < AHEAD; ++i) {
+      if constexpr (MB)
+        rf[i] = carry[i];
+      else
+        rf[i].load(raddr(i));
+    }
+    const unsigned char* knext = smem_raw + ((ph + 2) % NR) * Cfg::KT_B;  // K_{t+2} (MB only)
     const bool mask_next = (t + 2) * ATT_BN > Lk;
     float nmc[QB], vmax[QB], pbuf[QB][8];
 #pragma unroll
@@ -691,7 +707,22 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
     bool moved = false;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      if (i + AHEAD < 32) rf[i + AHEAD].load(raddr(i + AHEAD));
+      if constexpr (MB) {
+        if (i == 24) {
+          // K_{t+2} and V_{t+1} (copied during the previous iteration) have landed; after the
+          // barrier every wave has finished its reads of K_{t+1} (last used in slot 23) and
+          // of V_t (its reads for slots 24..31 were issued by slot 23 and are waited here),
+          // the stages the next iteration refills
+          att_wait_vmcnt<INFLIGHT>();
+          att_barrier_lds();
+        }
+        if (i + AHEAD < 32)
+          rf[i + AHEAD].load(raddr(i + AHEAD));
+        else
+          carry[i + AHEAD - 32].load(knext + koff[i + AHEAD - 32]);
+      } else {
+        if (i + AHEAD < 32) rf[i + AHEAD].load(raddr(i + AHEAD));
+      }
       if constexpr (SM) {
         // Static offset: no row maxima, so the only VALU work is one exp2 (and its sum) per
         // score, spread over every slot.  The two waves of a SIMD start each tile together
@@ -816,15 +847,19 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (moved) scale_o();
-    att_wait_vmcnt<INFLIGHT>();  // K_{t+2} and V_{t+1} have landed
-    att_barrier_lds();
+    if constexpr (!MB) {
+      att_wait_vmcnt<INFLIGHT>();  // K_{t+2} and V_{t+1} have landed
+      att_barrier_lds();
+    }
   };
-  static_assert(NR == 2 || NR == 4, "ring depth");
+  static_assert(NR == 2 || NR == 4 || (NR == 3 && SM), "ring depth");
   for (int t = 0; t < n; t += NR) {
     iter(t, 0);
     if (t + 1 < n) iter(t + 1, 1);
-    if constexpr (NR == 4) {
+    if constexpr (NR >= 3) {
       if (t + 2 < n) iter(t + 2, 2);
+    }
+    if constexpr (NR == 4) {
       if (t + 3 < n) iter(t + 3, 3);
     }
   }
@@ -1360,7 +1395,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
         return launch_attn_wide<128, WIDE_NR, 1, 4>(a, st);
       if (a.kpart && a.fallback && a.scale_log2 == 1.0f) {
         // static offset, then the running-maximum kernel on the workgroups it flagged
-        hipError_t e = launch_attn_wide<128, WIDE_NR, WIDE_QB, WIDE_NW, true>(a, st);
+        hipError_t e = launch_attn_wide<128, WIDE_NR_SM, WIDE_QB, WIDE_NW, true>(a, st);
         if (e != hipSuccess) return e;
         AttnArgs b = a;
         b.only = a.fallback;
