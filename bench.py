@@ -30,16 +30,17 @@ CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 # L2 <-> memory bytes of one self-attention launch (the static-offset kernel plus its flagged-workgroup
 # pass), from two counter-collection runs of
 # `bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-cache-modes --no-vae --no-qk8 --block-configs "" --calib-copy`
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, means over the 60 launches of each kernel, summed), each
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, means over the launches of each kernel, summed), each
 # scaled by known/counted bytes of the 1 GiB calibration copy in the same run.  Valid only for the kernel
 # sources they were taken on (checked by hash).
 ATTN_COUNTERS = {
-    "fetch_kib": 885003.13 + 117.00, "fetch_scale": 1048576 / 524302.88,
-    "write_kib": 196663.41 + 0.0, "write_scale": 1048576 / 1048576.0,
+    "fetch_kib": 885137.94 + 117.01, "fetch_scale": 1048576 / 524302.67,
+    "write_kib": 196656.0 + 0.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "e158d893c470c7ecfeb58628f3e2400414b8ae6a44ae575c2a19ccf86ec0554c",
+    "sha256": "71fe25bdc927c9e536c06f143fc3c1ef6ac5c863ed3982dbeac90611a10ae348",
 }
+
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"
 
 
@@ -528,7 +529,7 @@ def main():
         "block_tflops": round(block_tflops, 2),
         "step_tflop": round(flops / 1e12, 3),
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 3) for k, v in kt.items()},
-        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_wide_kernel<128,2,1,8,true>, static offset, and its flagged-workgroup pass)",
+        "roofline": {"bound": "mfma", "kernel": "self-attention (attn_self_wide_kernel<128,3,1,8,true>, static offset, and its flagged-workgroup pass)",
                      "achieved": round(attn_achieved, 2), "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / MI355X_BF16_TFLOPS, 4), "traffic": attn_traffic_bytes(),
                      "traffic_unit": "bytes per launch (L2-memory fetch + write counters)",
