@@ -1640,7 +1640,8 @@ hipError_t launch_by_n(const GemmArgs& g, hipStream_t st) {
         // gains 10% on 8 waves (4 waves spill its v^T staging); FFN1+GELU and a long-K residual
         // GEMM (FFN2, K = 8960) run best on 4 waves of 128x128 (two thirds of the LDS fragment
         // reads per MFMA), while the short-K residual GEMMs (K = 1536), whose epilogue
-        // dominates, stay on 8 waves of 32x32x16 (the 4-wave 16x16 form is 2% slower there)
+        // dominates, stay on 8 waves of 32x32x16 (the 4-wave and the 8-wave 16x16 forms are
+        // 2% and 1% slower there)
         if constexpr (EPI == EPI_PACK)
           return launch_cfg<T, 256, 256, 4, 2, 3, 128, 1, LOADER, EPI, 16>(g, st);
         if constexpr (EPI == EPI_STORE_GELU)
