@@ -18,6 +18,12 @@
  * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *   null stream) and the call returns without synchronising.  Faults of the
  *   enqueued kernels surface at the caller's next synchronisation.
+ * - Apart from a one-time device check and kernel attribute setup on the first
+ *   call on a device, a call enqueues only kernel launches and device-to-device
+ *   copies (and, while the measurement hook is enabled, its event pairs): once
+ *   an entry point has run eagerly it can be captured into a HIP graph, which
+ *   replays it with the scalars of the capture (timestep, step size, guide
+ *   scale).
  * - Every argument is validated before anything is enqueued; a call that
  *   returns an error has no side effect.
  * - Weight matrices use the Linear layout [out][in], row-major, in the mode's
