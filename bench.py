@@ -190,6 +190,70 @@ def vae_flops(vcfg) -> float:
     return total
 
 
+def time_vendor_gemms(cfg: S.WanConfig, reps: int = 10) -> dict:
+    """The step's projections through torch.nn.functional.linear (hipBLASLt) on the same shapes (CFG batch 2,
+    M = 2L rows), alone and followed by the work this library's GEMM epilogues fuse, done as separate torch
+    passes: GELU (erf) after FFN1; the gated float32 residual x += g * y after FFN2 and the output projections;
+    RoPE on q and k and the head-major q / k / transposed-v layout after QKV.  Random bf16 operands; ms per
+    launch, timed with events on torch's stream.  A measurement of the vendor library, not a path of this
+    library."""
+    import torch
+    import torch.nn.functional as F
+    dev, bf = "cuda", torch.bfloat16
+    L, D, Fd, H = cfg.seq_len, cfg.dim, cfg.ffn_dim, cfg.heads
+    hd, M = D // H, 2 * cfg.seq_len
+    g = torch.Generator(device=dev).manual_seed(7)
+
+    def rnd(*shape, dtype=bf, scale=0.02):
+        return (torch.randn(*shape, device=dev, generator=g, dtype=torch.float32) * scale).to(dtype)
+
+    m, hbuf = rnd(M, D, scale=1.0), rnd(M, Fd, scale=0.1)
+    x = rnd(M, D, dtype=torch.float32, scale=1.0)
+    gate = rnd(D, dtype=torch.float32, scale=0.1)
+    w = {"qkv": rnd(3 * D, D), "o": rnd(D, D), "ffn1": rnd(Fd, D), "ffn2": rnd(D, Fd)}
+    b = {k: rnd(v.shape[0]) for k, v in w.items()}
+    ang = torch.rand(L, hd // 2, device=dev, generator=g) * 6.28
+    cos, sin = torch.cos(ang).to(bf), torch.sin(ang).to(bf)
+
+    def rope(t):  # (2, L, H, hd) -> rotated adjacent pairs
+        t2 = t.view(2, L, H, hd // 2, 2)
+        c, s_ = cos.view(1, L, 1, hd // 2), sin.view(1, L, 1, hd // 2)
+        return torch.stack((t2[..., 0] * c - t2[..., 1] * s_, t2[..., 0] * s_ + t2[..., 1] * c), -1).view(2, L, H, hd)
+
+    def qkv_epi(y):
+        y = y.view(2, L, 3, H, hd)
+        q = rope(y[:, :, 0]).permute(0, 2, 1, 3).contiguous()
+        k = rope(y[:, :, 1]).permute(0, 2, 1, 3).contiguous()
+        vt = y[:, :, 2].permute(0, 2, 3, 1).contiguous()
+        return q, k, vt
+
+    cases = {
+        "qkv": (lambda: F.linear(m, w["qkv"], b["qkv"]), qkv_epi, 2 * M * D * 3 * D),
+        "o_proj": (lambda: F.linear(m, w["o"], b["o"]), lambda y: x.addcmul_(gate, y), 2 * M * D * D),
+        "ffn1": (lambda: F.linear(m, w["ffn1"], b["ffn1"]), lambda y: F.gelu(y), 2 * M * D * Fd),
+        "ffn2": (lambda: F.linear(hbuf, w["ffn2"], b["ffn2"]), lambda y: x.addcmul_(gate, y), 2 * M * Fd * D),
+    }
+    out = {}
+    for name, (gemm, epi, flop) in cases.items():
+        res = {}
+        for label, fn in (("gemm_ms", gemm), ("gemm_plus_epilogue_ms", lambda: epi(gemm()))):
+            for _ in range(2):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(reps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            res[label] = round(ev[0].elapsed_time(ev[1]) / reps, 4)
+        res["gemm_tflops"] = round(flop / (res["gemm_ms"] * 1e-3) / 1e12, 1)
+        out[name] = res
+    del m, hbuf, x, w
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_vae(name: str = "vae_480p", reps: int = 3) -> dict:
     """Whole-video decode of the 81-frame 480p latent (one call), timed with torch events."""
     import torch
@@ -335,6 +399,9 @@ def main():
     ap.add_argument("--no-qk8", action="store_true", help="skip timing the step in the 8-bit forms")
     ap.add_argument("--no-vae", action="store_true", help="skip timing the 480p x 81-frame VAE decode")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
+    ap.add_argument("--vendor-gemms", action="store_true",
+                    help="also time the step's projections through hipBLASLt (torch), alone and with their "
+                         "epilogue work as separate passes (reported under 'vendor_gemms')")
     ap.add_argument("--vae-only", action="store_true",
                     help="time only the VAE decode and print its JSON object (for profiling runs)")
     ap.add_argument("--block-configs", default="wan13b_block,wan14b_720p_block,wan14b_i2v_block",
@@ -572,6 +639,9 @@ def main():
         for name in [c for c in args.block_configs.split(",") if c]:
             print(f"[bench] block {name}", file=sys.stderr, flush=True)
             out["blocks"][name] = time_block(S.get_config(name))
+    if args.vendor_gemms:
+        print("[bench] vendor GEMMs", file=sys.stderr, flush=True)
+        out["vendor_gemms"] = time_vendor_gemms(cfg)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)
