@@ -668,7 +668,9 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
   // last tile S(n) is computed from a stale stage but masked out entirely.
   // `ph` = t % NR, a literal after inlining, so every LDS offset is an immediate.
   // A scheduling barrier closes every slot; values consumed in a later slot are
-  // pinned where they are produced.
+  // pinned where they are produced.  The static-offset form orders its slots
+  // differently (see the slot loop) and, with three-stage rings, synchronises the
+  // workgroup at slot 24 instead of at the end of the iteration.
   auto iter = [&](int t, int ph) {
     const int kst = (ph + 1) % NR, vst = ph;
     issue_k(min(t + NR, n - 1), ph);
