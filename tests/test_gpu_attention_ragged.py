@@ -78,3 +78,31 @@ def test_self_attention_static_offset_fallback(qk8):
     err = inc_err(got[:, rows], ref, x[:, rows])
     print(f"L={L} planted large-norm key qk8={qk8}: rel err {err:.3e} over {len(rows)} rows")
     assert err <= TOL["bf16"]
+
+
+# Short sequences reach the static-offset kernel through the batch: 43 videos x 12 heads give 516
+# 256-query workgroups at one query tile each.  That kernel's three-stage K / V^T rings then hold
+# more stages than there are key tiles (the copies past the last tile are clamped to it and the
+# scores past L masked, the next tile's first K fragments read from a clamped stage):
+#   64 = (1, 8, 8): one key tile; 130 = (2, 5, 13): three tiles, 2 keys in the last;
+#   195 = (3, 5, 13): four tiles, 3 keys in the last.
+SHORT = {64: (1, 8, 8), 130: (2, 5, 13), 195: (3, 5, 13)}
+
+
+@pytest.mark.parametrize("L", sorted(SHORT))
+def test_self_attention_few_key_tiles_static_offset(L):
+    f, h, w_ = SHORT[L]
+    base = S.get_config("wan13b_block")
+    cfg = base.with_(name=f"wan13b_b43_L{L}", seed_base=90 + L % 11, batch=43, frames=f, height=2 * h,
+                     width=2 * w_, qk_std=float(np.sqrt(4.0 / base.dim)))
+    assert cfg.seq_len == L and (L + 255) // 256 * cfg.heads * cfg.batch >= 512
+    announce(f"self-attention few key tiles L={L} batch={cfg.batch} grid={cfg.grid}")
+    w, x, mod, ctx = block_case(cfg)
+    w, mod = self_attention_only(cfg, w, mod)
+    rows = sample_rows(L, 10, seed=L)
+    got = gpu_block(cfg, w, x, mod, ctx)
+    assert np.all(np.isfinite(got))
+    ref = O.dit_block(x, mod, ctx, w, cfg.heads, cfg.grid, 0, rows=rows)
+    err = inc_err(got[:, rows], ref, x[:, rows])
+    print(f"L={L} batch {cfg.batch}: rel err {err:.3e} over {len(rows)} rows of every video")
+    assert err <= TOL["bf16"]

@@ -1030,7 +1030,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       constexpr int SP = BN + 16;
       static_assert((size_t)BM * SP * sizeof(T) <= C::LDS_BYTES, "bf16 staging");
       T* stage16 = reinterpret_cast<T*>(smem_raw);
-      const bool is_k = sec0 != 0;
+      const bool is_k = n0 >= g.nq;  // (a K / V-only packing GEMM has nq = 0)
       const int b = m0 / g.c_rpb, t0 = m0 - b * g.c_rpb;
       const int valid = g.c_valid > 0 ? g.c_valid : g.c_rpb;
       const float qsc = is_k ? 1.0f : g.q_scale;
