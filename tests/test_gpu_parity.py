@@ -198,6 +198,25 @@ def test_block_14b_full_size_sampled_rows(name):
     assert err <= TOL["bf16"]
 
 
+def test_block_14b_i2v_two_videos_equal_single_video_runs():
+    """The 14B I2V block over two videos at once (the CFG batch of a step) against two one-video
+    calls on the same inputs: bit for bit (every output sums the same products in the same order
+    whatever the tile it falls in).  With two videos the text and image K / V projections have
+    160 tiles of 256x256 and take the 16x16 packing form without a q section, which no one-video
+    shape reaches."""
+    cfg = S.get_config("wan14b_i2v_block").with_(batch=2)
+    announce("block wan14b_i2v two videos against one-video runs")
+    w, x, mod, ctx = block_case(cfg)
+    both = gpu_block(cfg, w, x, mod, ctx)
+    assert np.all(np.isfinite(both))
+    one = cfg.with_(batch=1)
+    for b in range(2):
+        single = gpu_block(one, w, x[b:b + 1], mod[b:b + 1], ctx[b:b + 1])
+        same = np.array_equal(single[0], both[b])
+        print(f"video {b}: two-video call equals the one-video call bitwise: {same}")
+        assert same
+
+
 # ----------------------------------------------------------------------------- head
 @pytest.mark.parametrize("name", ["toy", "mid_bf16"])
 def test_head(name):
