@@ -32,14 +32,14 @@ CALIB_COPY_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 # `bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-cache-modes --no-vae --no-qk8 --block-configs "" --calib-copy`
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, means over the launches of each kernel, summed), each
 # scaled by known/counted bytes of the 1 GiB calibration copy in the same run.  Valid only for the kernel
-# sources they were taken on (checked by hash; a later comment-only edit was re-hashed after checking that the
+# sources they were taken on (checked by hash; later comment and static_assert edits were re-hashed after checking that the
 # generated device code is unchanged).
 ATTN_COUNTERS = {
     "fetch_kib": 885137.94 + 117.01, "fetch_scale": 1048576 / 524302.67,
     "write_kib": 196656.0 + 0.0, "write_scale": 1048576 / 1048576.0,
     "sources": ("video_diffusion_transformer_forward_amd/csrc/attention.hip",
                 "video_diffusion_transformer_forward_amd/csrc/common.h"),
-    "sha256": "bcd7e13e9a8da5161bd6257f91c6619ebe0d0601cd8f59bfd6bfac9ff5658240",
+    "sha256": "7f8899957fe59dc0507d84bb809b526b266f2f2fd8da38a75f00fecdf42fbb13",
 }
 
 METRIC = "DiT block TFLOP/s (%bf16 MFMA peak) + ms/denoise step, 1.3B @ 480p×81f"

@@ -690,6 +690,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a) {
       return vbase + ((i - 16) % 4) * VBLK_B + voff[(i - 16) / 4];
     };
     constexpr int AHEAD = 8;
+    static_assert(!MB || AHEAD == 8, "carry holds the 8 reads issued in slots 24..31");
     Chunk<T> rf[32];
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) {
