@@ -460,6 +460,33 @@ def _depth_sweep(base, depths, rows_fn=None):
     return errs
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("i2v", [False, True], ids=["t2v", "i2v"])
+def test_step_14b_width_short_sequence_fp32(i2v):
+    """A CFG step at the 14B width (D = 5120, 40 heads of 128, FFN 13824, 512 text tokens; I2V: 36
+    input channels and 257 image tokens, decoupled cross-attention) over a short latent (grid
+    (2, 8, 12), L = 192), two blocks, in the float32 mode against the oracle over the whole output.
+    In bf16 this input sits beyond the 1e-2 bar for any bf16-operand computation: rounding every
+    GEMM and attention operand of the float64 oracle to bf16, and nothing else, moves the step by
+    1.05e-2 (the synthetic N(0, 0.02) weights give logits of std about 2 at this width), and the
+    bf16 library measures 1.02-1.16e-2 here.  The bf16 form of the K / V-only packing GEMM this
+    shape reaches is checked bit for bit by test_block_14b_i2v_two_videos_equal_single_video_runs."""
+    extra = {"in_ch": 36, "img_len": 257} if i2v else {}
+    cfg = S.get_config("wan13b_step").with_(name="wan14b_step_short", seed_base=61, dim=5120, heads=40,
+                                            ffn_dim=13824, frames=2, height=16, width=24, n_blocks=2, mode="fp32",
+                                            **extra)
+    announce(f"step 14B width short sequence fp32 i2v={i2v}")
+    mw = S.model_weights(cfg)
+    bw = [S.block_weights(cfg, b) for b in range(cfg.n_blocks)]
+    z, cond = S.latent(cfg), S.condition(cfg)
+    cc, cn = S.context(cfg, "cond"), S.context(cfg, "null")
+    got = gpu_step(cfg, mw, bw, z, cond, cc, cn, cfg.timestep, cfg.dt, cfg.guide_scale)
+    ref = O.denoise_step(z, cond, cc, cn, mw, bw, cfg.heads, cfg.timestep, cfg.dt, cfg.guide_scale, cfg.img_len)
+    err = inc_err(got, ref, z)
+    print(f"14B-width step fp32 i2v={i2v}: rel err of dt*v {err:.3e}")
+    assert err <= TOL["fp32"]
+
+
 def test_step_30_blocks_against_oracle_by_depth():
     """The CFG step with 30 distinct blocks (the 1.3B model's depth) at the mid shape
     (L = 180, D = 256, head dim 128) against the oracle, and how the bf16 error grows
